@@ -1,0 +1,160 @@
+"""Benchmark of the KDA chunked forward (one libkda kda_chunk_fwd call = one step of
+the whole hot path: gate, WY stage, state passing, output) on one MI355X.
+
+Default workload: B=4, H=32, T=16384, K=V=128, chunk 64, bf16 activations, fp32
+state, synthetic seeded inputs resident in HBM before the timed region.
+Prints one JSON line: head-tokens/s (B*H*T per second), the roofline of the fused
+kernel (algorithmic HBM bytes per launch / measured launch time vs 8 TB/s) and the
+f64 CPU oracle timed on a bounded sample of the same workload.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from concurrent.futures import ProcessPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+METRIC = "KDA chunked-forward tokens/s (B·H·T/s) + % of roofline, H=32,K=V=128,T=16k"
+
+
+def algorithmic_bytes(wl) -> int:
+    """HBM bytes one kda_chunk_fwd call must move at minimum: read q, k, z, v, beta
+    and the initial state once, write o and the final state once (A_log, dt_bias
+    are negligible but counted)."""
+    es = 2 if wl.dtype == "bf16" else 4
+    ht = wl.B * wl.H * wl.T
+    acts = ht * (3 * wl.K + wl.V + 1) * es + ht * wl.V * es
+    state = 2 * wl.B * wl.H * wl.K * wl.V * 4
+    params = wl.H * 4 + wl.H * wl.K * 4
+    return acts + state + params
+
+
+def _oracle_head(args):
+    """CPU baseline worker: the f64 oracle's token recurrence on one head."""
+    wl_name, b, h = args
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    import kda_synth as ks
+    from oracle import kda_ref as R
+    wl = ks.WORKLOADS[wl_name]
+    A_log, dt_bias = ks.head_params(wl)
+    sl = ks.head_slice(wl, b, h)
+    t0 = time.perf_counter()
+    g, _ = R.gate(sl["z"][None, None], A_log[h:h + 1], dt_bias[h:h + 1])
+    R.recurrent(sl["q"][None, None], sl["k"][None, None], sl["v"][None, None], g, sl["beta"][None, None],
+                sl["state_in"][None, None])
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(wl, n_heads: int, workers: int) -> dict:
+    heads = [(i // wl.H % wl.B, i % wl.H) for i in range(n_heads)]
+    t0 = time.perf_counter()
+    with ProcessPoolExecutor(workers) as ex:
+        list(ex.map(_oracle_head, [(wl.name, b, h) for b, h in heads]))
+    wall = time.perf_counter() - t0
+    return {"value": n_heads * wl.T / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": "%d of %d heads at full T=%d (f64 numpy token recurrence, one head per process, "
+                      "%.1f s wall)" % (n_heads, wl.B * wl.H, wl.T, wall)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_long.json"),
+                    help="HBM traffic per launch measured by rocprofv3 counters (if present)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (heads shard across GPUs "
+              "with no communication; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_47_amd as kda
+    import kda_synth as ks
+
+    wl = ks.WORKLOADS[args.workload]
+    if wl.adjoint:
+        raise SystemExit("the benchmark times the forward; pick a forward workload")
+    print("bench: generating %s (%s)" % (wl.name, wl.desc), file=sys.stderr, flush=True)
+    x = ks.generate(wl)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    d = {n: torch.from_numpy(x[n]).to(dev).to(dt) for n in ("q", "k", "v", "z", "beta")}
+    A_log = torch.from_numpy(x["A_log"]).to(dev)
+    dt_bias = torch.from_numpy(x["dt_bias"]).to(dev)
+    state_in = torch.from_numpy(x["state_in"]).to(dev)
+    del x
+    o = torch.empty((wl.B, wl.H, wl.T, wl.V), dtype=dt, device=dev)
+    state_out = torch.empty_like(state_in)
+    scale = kda.read_scale(wl.K)
+
+    def step():
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["z"], A_log, dt_bias, d["beta"], state_in, scale=scale,
+                      chunk=wl.chunk, out=o, state_out=state_out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    if not (torch.isfinite(o[0, 0].float()).all() and torch.isfinite(state_out).all()):
+        raise SystemExit("non-finite output")
+
+    ms_per_step = wall * 1e3 / args.steps
+    avg_kernel_ms = float(np.mean(kern_ms))
+    tokens = wl.B * wl.H * wl.T
+    nbytes = algorithmic_bytes(wl)
+    achieved = nbytes / (avg_kernel_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            if tj.get("workload") == wl.name:
+                traffic = tj.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "kda::chunk_fwd_kernel", "algorithmic_bytes_per_launch": nbytes,
+            "avg_kernel_ms": round(avg_kernel_ms, 4), "min_kernel_ms": round(float(np.min(kern_ms)), 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        workers = min(16, len(os.sched_getaffinity(0)))
+        print("bench: CPU oracle baseline on %d heads" % workers, file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, n_heads=workers, workers=workers)
+    out = {
+        "metric": METRIC, "value": round(tokens / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "K": wl.K, "V": wl.V, "chunk": wl.chunk,
+                   "activations": wl.dtype, "state": "f32", "global_batch": wl.B, "seq_len": wl.T,
+                   "parallelism": "single-gpu"},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

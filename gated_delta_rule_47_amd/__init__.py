@@ -1,0 +1,186 @@
+"""Kimi Delta Attention (KDA) on AMD Instinct MI355X: Python binding of libkda.
+
+Argument marshalling only: every function checks the tensors, passes their device
+pointers and the current HIP stream to the C ABI declared in include/kda.h, and
+raises KdaError on a non-zero status.  All arithmetic runs in the library's HIP
+kernels; there is no Python or CPU implementation behind these functions.
+
+Layouts (head-major, contiguous): q, k, z (B,H,T,K); v, o (B,H,T,V); beta (B,H,T);
+state (B,H,K,V) float32; A_log (H,) float32; dt_bias (H,K) float32.  Activations are
+float32 or bfloat16 (one dtype for q, k, v, z, beta and o).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+__all__ = ["KdaError", "read_scale", "gate", "chunk_fwd", "recurrent_step", "chunk_bwd",
+           "chunk_bwd_workspace_bytes", "counters", "status_string", "library_path"]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (fn, status_string(status), status))
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def status_string(status: int) -> str:
+    return _lib.load().kda_status_string(int(status)).decode()
+
+
+def read_scale(K: int) -> float:
+    """FLA's default read scale K**-0.5, as the library computes it."""
+    return float(_lib.load().kda_read_scale(int(K)))
+
+
+def counters() -> dict:
+    lib = _lib.load()
+    n = lib.kda_get_counters(None, 0)
+    arr = (ctypes.c_ulonglong * n)()
+    lib.kda_get_counters(arr, n)
+    return {name: int(arr[i]) for i, name in enumerate(_lib.COUNTER_NAMES[:n])}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return _lib.KDA_F32
+    if t.dtype == torch.bfloat16:
+        return _lib.KDA_BF16
+    raise TypeError("activations must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check_f32(name, t, shape):
+    if t is None:
+        return
+    if t.dtype != torch.float32:
+        raise TypeError("%s must be float32" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _call(fn_name, *args):
+    st = getattr(_lib.load(), fn_name)(*args)
+    if st != _lib.KDA_OK:
+        raise KdaError(fn_name, st)
+
+
+def gate(z, A_log, dt_bias=None, want_alpha=True):
+    """g = -exp(clamp(A_log)) * softplus(z + dt_bias) and alpha = exp(g), float32."""
+    B, H, T, K = z.shape
+    _check_f32("A_log", A_log, (H,))
+    _check_f32("dt_bias", dt_bias, (H, K))
+    g = torch.empty(z.shape, dtype=torch.float32, device=z.device)
+    alpha = torch.empty_like(g) if want_alpha else None
+    _call("kda_gate", _ptr(z), _ptr(A_log), _ptr(dt_bias), _ptr(g), _ptr(alpha), B, H, T, K,
+          _dtype_code(z), _stream(z.device))
+    return g, alpha
+
+
+def _check_acts(q, k, v, z, beta):
+    B, H, T, K = q.shape
+    V = v.shape[-1]
+    for name, t, shape in (("k", k, (B, H, T, K)), ("z", z, (B, H, T, K)), ("v", v, (B, H, T, V)),
+                           ("beta", beta, (B, H, T))):
+        if tuple(t.shape) != shape:
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), shape))
+        if t.dtype != q.dtype:
+            raise TypeError("%s has dtype %s, q has %s" % (name, t.dtype, q.dtype))
+    return B, H, T, K, V
+
+
+def chunk_fwd(q, k, v, z, A_log, dt_bias, beta, state_in=None, scale=None, chunk=64,
+              output_state=True, out=None, state_out=None):
+    """Chunked KDA forward.  Returns (o, state_out); state_out is None when
+    output_state is False.  scale=None means K**-0.5."""
+    B, H, T, K, V = _check_acts(q, k, v, z, beta)
+    _check_f32("A_log", A_log, (H,))
+    _check_f32("dt_bias", dt_bias, (H, K))
+    _check_f32("state_in", state_in, (B, H, K, V))
+    if scale is None:
+        scale = read_scale(K)
+    o = out if out is not None else torch.empty((B, H, T, V), dtype=q.dtype, device=q.device)
+    if output_state and state_out is None:
+        state_out = torch.empty((B, H, K, V), dtype=torch.float32, device=q.device)
+    if not output_state:
+        state_out = None
+    _call("kda_chunk_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(dt_bias), _ptr(beta),
+          _ptr(state_in), float(scale), int(chunk), _ptr(o), _ptr(state_out), B, H, T, K, V,
+          _dtype_code(q), _stream(q.device))
+    return o, state_out
+
+
+def recurrent_step(q, k, v, z, A_log, dt_bias, beta, state, scale=None, out=None):
+    """One decode token per (b,h): q,k,z (B,H,K), v (B,H,V), beta (B,H).  Updates
+    `state` (B,H,K,V) float32 in place and returns o (B,H,V)."""
+    B, H, K = q.shape
+    V = v.shape[-1]
+    for name, t, shape in (("k", k, (B, H, K)), ("z", z, (B, H, K)), ("v", v, (B, H, V)), ("beta", beta, (B, H))):
+        if tuple(t.shape) != shape:
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), shape))
+        if t.dtype != q.dtype:
+            raise TypeError("%s has dtype %s, q has %s" % (name, t.dtype, q.dtype))
+    _check_f32("A_log", A_log, (H,))
+    _check_f32("dt_bias", dt_bias, (H, K))
+    _check_f32("state", state, (B, H, K, V))
+    if scale is None:
+        scale = read_scale(K)
+    o = out if out is not None else torch.empty((B, H, V), dtype=q.dtype, device=q.device)
+    _call("kda_recurrent_step", _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(dt_bias), _ptr(beta),
+          _ptr(state), float(scale), _ptr(o), B, H, K, V, _dtype_code(q), _stream(q.device))
+    return o
+
+
+def chunk_bwd_workspace_bytes(B, H, T, K, V, chunk=64) -> int:
+    return int(_lib.load().kda_chunk_bwd_workspace_bytes(B, H, T, K, V, chunk))
+
+
+def chunk_bwd(q, k, v, z, A_log, dt_bias, beta, state_in, d_o, d_state_out=None, scale=None, chunk=64,
+              workspace=None):
+    """Gradients of sum(o*d_o) + sum(state_out*d_state_out); float32 activations.
+    Returns dict(dq, dk, dv, dg, dbeta, dstate_in), all float32."""
+    B, H, T, K, V = _check_acts(q, k, v, z, beta)
+    _check_f32("A_log", A_log, (H,))
+    _check_f32("dt_bias", dt_bias, (H, K))
+    _check_f32("state_in", state_in, (B, H, K, V))
+    _check_f32("d_state_out", d_state_out, (B, H, K, V))
+    if tuple(d_o.shape) != (B, H, T, V) or d_o.dtype != q.dtype:
+        raise ValueError("d_o must match o's shape and dtype")
+    if scale is None:
+        scale = read_scale(K)
+    need = chunk_bwd_workspace_bytes(B, H, T, K, V, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dq=torch.empty((B, H, T, K), **f32), dk=torch.empty((B, H, T, K), **f32),
+               dv=torch.empty((B, H, T, V), **f32), dg=torch.empty((B, H, T, K), **f32),
+               dbeta=torch.empty((B, H, T), **f32), dstate_in=torch.empty((B, H, K, V), **f32))
+    _call("kda_chunk_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(dt_bias), _ptr(beta),
+          _ptr(state_in), float(scale), int(chunk), _ptr(d_o), _ptr(d_state_out), _ptr(out["dq"]),
+          _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dstate_in"]),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, T, K, V, _dtype_code(q),
+          _stream(dev))
+    return out

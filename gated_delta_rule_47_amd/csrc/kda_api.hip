@@ -1,0 +1,222 @@
+// C ABI of libkda (see include/kda.h): argument checks, dispatch to kernel
+// instances, status codes and call counters.  No allocation, no printing, no
+// exceptions across the boundary, no fallback path.
+#include <atomic>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+static std::atomic<unsigned long long> g_counters[KDA_NUM_COUNTERS];
+
+static int reject(int status) {
+  g_counters[KDA_COUNTER_REJECTED].fetch_add(1, std::memory_order_relaxed);
+  return status;
+}
+
+static bool valid_dim(int d) { return d == 8 || d == 16 || d == 32 || d == 64 || d == 128; }
+static bool valid_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+static size_t esize(int dtype) { return dtype == KDA_BF16 ? 2 : 4; }
+
+// True when [a, a+na) and [b, b+nb) share a byte.
+static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+bool fwd_plan(bool bf16, int K, int V, int chunk, FwdPlan* p) {
+  if (!valid_dim(K) || !valid_dim(V) || !valid_chunk(chunk)) return false;
+  if (bf16) {
+    p->KD = K < 32 ? 32 : K;
+    p->VT = V < 16 ? 16 : (V > 64 ? 64 : V);
+    p->C = chunk;
+  } else {
+    p->KD = K < 16 ? 16 : K;
+    const int vtmax = p->KD >= 64 ? 32 : 64;
+    p->VT = V < 16 ? 16 : (V > vtmax ? vtmax : V);
+    p->C = (p->KD == 128 && chunk > 32) ? 32 : chunk;
+  }
+  return true;
+}
+
+static hipError_t launch_fwd(bool bf16, const FwdPlan& p, const void* q, const void* k, const void* v, const void* z,
+                             const float* A_log, const float* dt_bias, const void* beta, const float* state_in,
+                             float scale, void* o, float* state_out, int B, int H, int T, int K, int V,
+                             hipStream_t s) {
+#define KDA_FWD(TYPE, KD_)                                                                                    \
+  return launch_chunk_fwd_kd<TYPE, KD_>(p.VT, p.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, o,     \
+                                         state_out, nullptr, B, H, T, K, V, s)
+  if (bf16) {
+    switch (p.KD) {
+      case 32: KDA_FWD(bf16_t, 32);
+      case 64: KDA_FWD(bf16_t, 64);
+      case 128: KDA_FWD(bf16_t, 128);
+    }
+  } else {
+    switch (p.KD) {
+      case 16: KDA_FWD(float, 16);
+      case 32: KDA_FWD(float, 32);
+      case 64: KDA_FWD(float, 64);
+      case 128: KDA_FWD(float, 128);
+    }
+  }
+#undef KDA_FWD
+  return hipErrorInvalidValue;
+}
+
+// Copies state_in to state_out (or zeroes it) for T == 0 with a plain copy kernel.
+__global__ void copy_state_kernel(const float* __restrict__ src, float* __restrict__ dst, long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src ? src[i] : 0.0f;
+}
+
+}  // namespace kda
+
+using namespace kda;
+
+extern "C" {
+
+float kda_read_scale(int K) { return K > 0 ? (float)(1.0 / __builtin_sqrt((double)K)) : 0.0f; }
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "null pointer";
+    case KDA_ERR_SHAPE: return "unsupported shape";
+    case KDA_ERR_DTYPE: return "unsupported dtype";
+    case KDA_ERR_CHUNK: return "unsupported chunk size";
+    case KDA_ERR_ALIAS: return "output aliases an input";
+    case KDA_ERR_HIP: return "HIP launch or runtime error";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int kda_get_counters(unsigned long long* out, int n) {
+  if (out) {
+    for (int i = 0; i < n && i < KDA_NUM_COUNTERS; ++i) out[i] = g_counters[i].load(std::memory_order_relaxed);
+  }
+  return KDA_NUM_COUNTERS;
+}
+
+int kda_gate(const void* z, const float* A_log, const float* dt_bias, float* g_out, float* alpha_out, int B, int H,
+             int T, int K, int dtype, void* stream) {
+  if (!A_log || (T != 0 && (!z || !g_out))) return reject(KDA_ERR_NULL);
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return reject(KDA_ERR_DTYPE);
+  if (B < 1 || H < 1 || T < 0 || K < 1) return reject(KDA_ERR_SHAPE);
+  const size_t n = (size_t)B * H * T * K;
+  if (overlap(g_out, n * 4, z, n * esize(dtype)) || overlap(alpha_out, n * 4, z, n * esize(dtype)) ||
+      overlap(g_out, n * 4, alpha_out, n * 4))
+    return reject(KDA_ERR_ALIAS);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dtype == KDA_BF16 ? launch_gate<bf16_t>(z, A_log, dt_bias, g_out, alpha_out, B, H, T, K, s)
+                                   : launch_gate<float>(z, A_log, dt_bias, g_out, alpha_out, B, H, T, K, s);
+  if (e != hipSuccess) return reject(KDA_ERR_HIP);
+  g_counters[KDA_COUNTER_GATE].fetch_add(1, std::memory_order_relaxed);
+  return KDA_OK;
+}
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* z, const float* A_log,
+                  const float* dt_bias, const void* beta, const float* state_in, float scale, int chunk, void* o,
+                  float* state_out, int B, int H, int T, int K, int V, int dtype, void* stream) {
+  if (!A_log || (T != 0 && (!q || !k || !v || !z || !beta || !o))) return reject(KDA_ERR_NULL);
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return reject(KDA_ERR_DTYPE);
+  if (B < 1 || H < 1 || T < 0 || !valid_dim(K) || !valid_dim(V)) return reject(KDA_ERR_SHAPE);
+  if (!valid_chunk(chunk)) return reject(KDA_ERR_CHUNK);
+  const size_t es = esize(dtype);
+  const size_t nk = (size_t)B * H * T * K * es, nv = (size_t)B * H * T * V * es, nb = (size_t)B * H * T * es;
+  const size_t ns = (size_t)B * H * K * V * 4;
+  const void* ins[] = {q, k, z};
+  for (const void* p : ins)
+    if (overlap(o, nv, p, nk)) return reject(KDA_ERR_ALIAS);
+  if (overlap(o, nv, v, nv) || overlap(o, nv, beta, nb) || overlap(o, nv, state_in, ns) ||
+      overlap(o, nv, state_out, ns))
+    return reject(KDA_ERR_ALIAS);
+  for (const void* p : ins)
+    if (overlap(state_out, ns, p, nk)) return reject(KDA_ERR_ALIAS);
+  if (overlap(state_out, ns, v, nv) || overlap(state_out, ns, beta, nb)) return reject(KDA_ERR_ALIAS);
+  if (state_out && state_in && state_out != state_in && overlap(state_out, ns, state_in, ns))
+    return reject(KDA_ERR_ALIAS);
+  FwdPlan plan;
+  if (!fwd_plan(dtype == KDA_BF16, K, V, chunk, &plan)) return reject(KDA_ERR_SHAPE);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (T == 0) {
+    if (state_out && state_out != state_in) {
+      const long long n = (long long)B * H * K * V;
+      hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, state_in, state_out,
+                         n);
+      e = hipGetLastError();
+    }
+  } else {
+    e = launch_fwd(dtype == KDA_BF16, plan, q, k, v, z, A_log, dt_bias, beta, state_in, scale, o, state_out, B, H, T,
+                   K, V, s);
+  }
+  if (e != hipSuccess) return reject(KDA_ERR_HIP);
+  g_counters[KDA_COUNTER_CHUNK_FWD].fetch_add(1, std::memory_order_relaxed);
+  return KDA_OK;
+}
+
+int kda_recurrent_step(const void* q, const void* k, const void* v, const void* z, const float* A_log,
+                       const float* dt_bias, const void* beta, float* state, float scale, void* o, int B, int H,
+                       int K, int V, int dtype, void* stream) {
+  if (!q || !k || !v || !z || !A_log || !beta || !state || !o) return reject(KDA_ERR_NULL);
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return reject(KDA_ERR_DTYPE);
+  if (B < 1 || H < 1 || !valid_dim(K) || !valid_dim(V)) return reject(KDA_ERR_SHAPE);
+  const size_t es = esize(dtype);
+  const size_t nk = (size_t)B * H * K * es, nv = (size_t)B * H * V * es, ns = (size_t)B * H * K * V * 4;
+  if (overlap(o, nv, q, nk) || overlap(o, nv, k, nk) || overlap(o, nv, z, nk) || overlap(o, nv, v, nv) ||
+      overlap(o, nv, beta, (size_t)B * H * es) || overlap(o, nv, state, ns) || overlap(state, ns, q, nk) ||
+      overlap(state, ns, k, nk) || overlap(state, ns, z, nk) || overlap(state, ns, v, nv))
+    return reject(KDA_ERR_ALIAS);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dtype == KDA_BF16
+                     ? launch_step<bf16_t>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, K, V, s)
+                     : launch_step<float>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, K, V, s);
+  if (e != hipSuccess) return reject(KDA_ERR_HIP);
+  g_counters[KDA_COUNTER_RECURRENT_STEP].fetch_add(1, std::memory_order_relaxed);
+  return KDA_OK;
+}
+
+size_t kda_chunk_bwd_workspace_bytes(int B, int H, int T, int K, int V, int chunk) {
+  if (B < 1 || H < 1 || T < 0) return 0;
+  return bwd_workspace_bytes(B, H, T, K, V, chunk);
+}
+
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z, const float* A_log,
+                  const float* dt_bias, const void* beta, const float* state_in, float scale, int chunk,
+                  const void* d_o, const float* d_state_out, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                  float* dstate_in, void* workspace, size_t workspace_bytes, int B, int H, int T, int K, int V,
+                  int dtype, void* stream) {
+  if (!A_log || !dstate_in ||
+      (T != 0 && (!q || !k || !v || !z || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta)))
+    return reject(KDA_ERR_NULL);
+  if (dtype != KDA_F32) return reject(KDA_ERR_DTYPE);
+  if (B < 1 || H < 1 || T < 0 || !valid_dim(K) || !valid_dim(V)) return reject(KDA_ERR_SHAPE);
+  if (!valid_chunk(chunk)) return reject(KDA_ERR_CHUNK);
+  const size_t need = bwd_workspace_bytes(B, H, T, K, V, chunk);
+  if (!workspace || workspace_bytes < need) return reject(KDA_ERR_WORKSPACE);
+  const size_t nk = (size_t)B * H * T * K * 4, nv = (size_t)B * H * T * V * 4, nb = (size_t)B * H * T * 4;
+  const size_t ns = (size_t)B * H * K * V * 4;
+  struct Buf { const void* p; size_t n; };
+  const Buf ins[] = {{q, nk}, {k, nk}, {v, nv}, {z, nk}, {beta, nb}, {state_in, ns}, {d_o, nv}, {d_state_out, ns},
+                     {workspace, need}};
+  const Buf outs[] = {{dq, nk}, {dk, nk}, {dv, nv}, {dg, nk}, {dbeta, nb}, {dstate_in, ns}};
+  for (const Buf& a : outs) {
+    for (const Buf& b : ins)
+      if (overlap(a.p, a.n, b.p, b.n)) return reject(KDA_ERR_ALIAS);
+    for (const Buf& b : outs)
+      if (&a != &b && overlap(a.p, a.n, b.p, b.n)) return reject(KDA_ERR_ALIAS);
+  }
+  hipError_t e = launch_chunk_bwd((const float*)q, (const float*)k, (const float*)v, (const float*)z, A_log, dt_bias,
+                                  (const float*)beta, state_in, scale, chunk, (const float*)d_o, d_state_out, dq, dk,
+                                  dv, dg, dbeta, dstate_in, workspace, B, H, T, K, V, (hipStream_t)stream);
+  if (e != hipSuccess) return reject(KDA_ERR_HIP);
+  g_counters[KDA_COUNTER_CHUNK_BWD].fetch_add(1, std::memory_order_relaxed);
+  return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,359 @@
+// Adjoint of the KDA forward (fp32): gradients of L = sum(o * d_o) + sum(S_T * d_S_T)
+// with respect to q, k, v, the log-decay g, beta and the initial state.
+//
+// Structure (the adjoint page's split into an intra-chunk part and a reverse
+// recurrence over chunks that carries dS):
+//   1. the fused chunked forward runs once and stores the state at every chunk
+//      start (the checkpoints);
+//   2. one workgroup per (batch, head, value tile) walks the chunks in reverse.
+//      For each chunk it recomputes the token states inside the chunk from the
+//      checkpoint (kept in a per-workgroup scratch: every thread reads back only
+//      the state elements it wrote), then runs the token-level reverse recurrence
+//         dS += q_hat do^T,  e = v - S'^T k,  de = beta dS^T k,
+//         dq = scale S_t do,  dk = beta dS e - S' de,  dv = de,  dbeta = k.dS e,
+//         dS' = dS - k de^T,  dg = alpha * rowsum(dS' * S_{t-1}),  dS = alpha dS'
+//      with S' = diag(alpha) S_{t-1} and S_t do = S' do + beta k (e.do);
+//   3. the row sums over value columns (dq, dk, dg and dS e) are partial per value
+//      tile; a last kernel adds the tiles in a fixed order and forms
+//      dbeta = k . (dS e).  Nothing uses atomics, so results are deterministic.
+//
+// Thread layout of step 2: thread (a, b) holds rows 4a..4a+3 and value columns
+// 4b..4b+3 of the K x VT tile.  Sums over columns are shuffles across the CB lanes
+// of a row block; sums over rows are shuffles inside the wave plus one LDS exchange
+// between the four waves per token.
+#include "kda_common.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+constexpr int kBwdVTMax = 32;
+
+__device__ __forceinline__ float xor_sum(float x, int lo, int hi) {
+  for (int m = lo; m < hi; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+template <int K, int VT, int CKMAX>
+__global__ void __launch_bounds__(256)
+bwd_reverse_kernel(const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+                   const float* __restrict__ z, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+                   const float* __restrict__ beta, float scale, const float* __restrict__ d_o,
+                   const float* __restrict__ d_state_out, const float* __restrict__ ckpt, float* __restrict__ scratch,
+                   float* __restrict__ part, float* __restrict__ dv, float* __restrict__ dstate_in, int H, int T,
+                   int V, int CK, int nck, int nvt) {
+  constexpr int CB = VT / 4, RB = K / 4, NTH = RB * CB;
+  static_assert(NTH <= 256, "tile too large for one workgroup");
+  __shared__ float sAl[CKMAX * K], sK[CKMAX * K], sQ[CKMAX * K];
+  __shared__ float sV[CKMAX * VT], sDO[CKMAX * VT], sB[CKMAX];
+  __shared__ float sRed[2][2][4][VT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool act = tid < NTH;
+  const int b = tid % CB;                 // every lane < CB of every wave names one column block
+  const int a = act ? tid / CB : 0;       // idle threads alias row block 0 and never store
+  const int bh = blockIdx.x / nvt, vt = blockIdx.x % nvt, h = bh % H, v0 = vt * VT;
+  const int BH = gridDim.x / nvt;
+  const float mult2 = gate_multiplier(A_log[h]) * kLog2e;
+  float* scr = scratch + (size_t)blockIdx.x * CKMAX * K * VT;
+
+  float dS[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dS[i][j] = (act && d_state_out) ? d_state_out[((size_t)bh * K + 4 * a + i) * V + v0 + 4 * b + j] : 0.0f;
+
+  // Sum of per-thread column partials p[0..3] over all rows of the tile.
+  auto col_reduce2 = [&](float (&p)[4], float (&p2)[4], int parity) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = act ? p[j] : 0.0f;
+      p2[j] = act ? p2[j] : 0.0f;
+      p[j] = xor_sum(p[j], CB, 64);
+      p2[j] = xor_sum(p2[j], CB, 64);
+    }
+    if (lane < CB) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sRed[parity][0][wave][4 * b + j] = p[j];
+        sRed[parity][1][wave][4 * b + j] = p2[j];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) { s0 += sRed[parity][0][w][4 * b + j]; s1 += sRed[parity][1][w][4 * b + j]; }
+      p[j] = s0;
+      p2[j] = s1;
+    }
+  };
+
+  int parity = 0;
+  for (int ci = nck - 1; ci >= 0; --ci) {
+    const int tc0 = ci * CK;
+    const int n = min(CK, T - tc0);
+    __syncthreads();
+    for (int idx = tid; idx < n * K; idx += 256) {
+      const int t = idx / K, c = idx % K;
+      const size_t g = ((size_t)bh * T + tc0 + t) * K + c;
+      const float x = z[g] + (dt_bias ? dt_bias[h * K + c] : 0.0f);
+      sAl[idx] = fast_exp2(-mult2 * softplus_f(x, true));
+      sK[idx] = k[g];
+      sQ[idx] = scale * q[g];
+    }
+    for (int idx = tid; idx < n * VT; idx += 256) {
+      const int t = idx / VT, j = idx % VT;
+      const size_t g = ((size_t)bh * T + tc0 + t) * V + v0 + j;
+      sV[idx] = v[g];
+      sDO[idx] = d_o[g];
+    }
+    for (int t = tid; t < n; t += 256) sB[t] = beta[(size_t)bh * T + tc0 + t];
+    const float* ck = ckpt + ((size_t)bh * nck + ci) * K * V;
+    float S[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[i][j] = act ? ck[(size_t)(4 * a + i) * V + v0 + 4 * b + j] : 0.0f;
+    __syncthreads();
+
+    // forward recompute: the states after tokens 0..n-2 of this chunk
+    for (int t = 0; t < n - 1; ++t) {
+      float rp[4] = {0.f, 0.f, 0.f, 0.f}, dummy[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float al = sAl[t * K + 4 * a + i], kk = sK[t * K + 4 * a + i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { S[i][j] *= al; rp[j] += S[i][j] * kk; }
+      }
+      col_reduce2(rp, dummy, parity);
+      parity ^= 1;
+      const float bt = sB[t];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float kk = bt * sK[t * K + 4 * a + i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[i][j] += kk * (sV[t * VT + 4 * b + j] - rp[j]);
+        if (act)
+          *reinterpret_cast<floatx4*>(scr + ((size_t)t * K + 4 * a + i) * VT + 4 * b) =
+              floatx4{S[i][0], S[i][1], S[i][2], S[i][3]};
+      }
+    }
+
+    // reverse over the chunk's tokens
+    for (int t = n - 1; t >= 0; --t) {
+      const size_t tok = (size_t)bh * T + tc0 + t;
+      float Sprev[4][4];                           // S_{t-1}, undecayed
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (t == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) Sprev[i][j] = act ? ck[(size_t)(4 * a + i) * V + v0 + 4 * b + j] : 0.0f;
+        } else {
+          floatx4 x = act ? *reinterpret_cast<const floatx4*>(scr + ((size_t)(t - 1) * K + 4 * a + i) * VT + 4 * b)
+                          : zero4();
+#pragma unroll
+          for (int j = 0; j < 4; ++j) Sprev[i][j] = x[j];
+        }
+      }
+      float al[4], kk[4], qh[4], vv[4], dov[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        al[i] = sAl[t * K + 4 * a + i];
+        kk[i] = sK[t * K + 4 * a + i];
+        qh[i] = sQ[t * K + 4 * a + i];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vv[j] = sV[t * VT + 4 * b + j];
+        dov[j] = sDO[t * VT + 4 * b + j];
+      }
+      const float bt = sB[t];
+      float ep[4] = {0.f, 0.f, 0.f, 0.f}, dep[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dS[i][j] += qh[i] * dov[j];              // dS += q_hat do^T
+          ep[j] += al[i] * Sprev[i][j] * kk[i];    // S'^T k, S' = diag(alpha) S_{t-1}
+          dep[j] += dS[i][j] * kk[i];              // dS^T k
+        }
+      col_reduce2(ep, dep, parity);
+      parity ^= 1;
+      float e[4], de[4], edo = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        e[j] = vv[j] - ep[j];
+        de[j] = bt * dep[j];
+        edo += e[j] * dov[j];
+      }
+      float sdo[4], dse[4], sde[4], dgp[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sdo[i] = 0.f; dse[i] = 0.f; sde[i] = 0.f; dgp[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float sd = al[i] * Sprev[i][j];
+          sdo[i] += sd * dov[j];
+          dse[i] += dS[i][j] * e[j];
+          sde[i] += sd * de[j];
+          const float dsd = dS[i][j] - kk[i] * de[j];    // dS' = dS - k de^T
+          dgp[i] += dsd * Sprev[i][j];
+          dS[i][j] = dsd;
+        }
+      }
+      // sums over this tile's value columns
+      edo = xor_sum(act ? edo : 0.f, 1, CB);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sdo[i] = xor_sum(sdo[i], 1, CB);
+        dse[i] = xor_sum(dse[i], 1, CB);
+        sde[i] = xor_sum(sde[i], 1, CB);
+        dgp[i] = xor_sum(dgp[i], 1, CB);
+      }
+      if (act && b == 0) {
+        float* pp = part + (((size_t)vt * BH + bh) * T + tc0 + t) * 4 * K;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = 4 * a + i;
+          pp[c] = scale * (sdo[i] + bt * kk[i] * edo);     // dq partial
+          pp[K + c] = bt * dse[i] - sde[i];                 // dk partial
+          pp[2 * K + c] = al[i] * dgp[i];                   // dg partial
+          pp[3 * K + c] = dse[i];                           // (dS e) partial, for dbeta
+        }
+      }
+      if (act && a == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dv[tok * V + v0 + 4 * b + j] = de[j];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dS[i][j] *= al[i];    // dS_{t-1} = diag(alpha) dS'
+    }
+  }
+  if (act) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dstate_in[((size_t)bh * K + 4 * a + i) * V + v0 + 4 * b + j] = dS[i][j];
+  }
+}
+
+// One wave per token row: add the value-tile partials in tile order.
+__global__ void __launch_bounds__(256)
+bwd_reduce_kernel(const float* __restrict__ part, const float* __restrict__ k, float* __restrict__ dq,
+                  float* __restrict__ dk, float* __restrict__ dg, float* __restrict__ dbeta, long long BHT, int K,
+                  int nvt) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= BHT) return;
+  float acc = 0.0f;
+  for (int c = lane; c < K; c += 64) {
+    float sq = 0.f, sk = 0.f, sg = 0.f, se = 0.f;
+    for (int t = 0; t < nvt; ++t) {
+      const float* pp = part + ((size_t)t * BHT + row) * 4 * K;
+      sq += pp[c];
+      sk += pp[K + c];
+      sg += pp[2 * K + c];
+      se += pp[3 * K + c];
+    }
+    dq[row * K + c] = sq;
+    dk[row * K + c] = sk;
+    dg[row * K + c] = sg;
+    acc += k[row * K + c] * se;
+  }
+  acc = xor_sum(acc, 1, 64);
+  if (lane == 0) dbeta[row] = acc;
+}
+
+// ------------------------------------------------------------------ host side
+struct BwdPlan {
+  FwdPlan fwd;
+  int VT, nvt, CK, nck;
+  size_t off_scratch, off_part, bytes;
+};
+
+static bool bwd_plan(int B, int H, int T, int K, int V, int chunk, BwdPlan* p) {
+  if (!fwd_plan(false, K, V, chunk, &p->fwd)) return false;
+  p->VT = V < kBwdVTMax ? V : kBwdVTMax;
+  p->nvt = V / p->VT;
+  p->CK = p->fwd.C;
+  p->nck = (T + p->CK - 1) / p->CK;
+  const size_t BH = (size_t)B * H;
+  const size_t ckpt = BH * p->nck * K * V * sizeof(float);
+  const int ckmax = K == 128 ? 32 : 64;
+  const size_t scratch = BH * p->nvt * (size_t)ckmax * K * p->VT * sizeof(float);
+  const size_t part = (size_t)p->nvt * BH * T * 4 * K * sizeof(float);
+  p->off_scratch = (ckpt + 255) / 256 * 256;
+  p->off_part = (p->off_scratch + scratch + 255) / 256 * 256;
+  p->bytes = p->off_part + part;
+  return true;
+}
+
+size_t bwd_workspace_bytes(int B, int H, int T, int K, int V, int chunk) {
+  BwdPlan p;
+  return bwd_plan(B, H, T, K, V, chunk, &p) ? p.bytes : 0;
+}
+
+template <int K, int VT>
+static hipError_t launch_rev(const BwdPlan& p, const float* q, const float* k, const float* v, const float* z,
+                             const float* A_log, const float* dt_bias, const float* beta, float scale, const float* d_o,
+                             const float* d_state_out, char* ws, float* dv, float* dstate_in, int B, int H, int T,
+                             int V, hipStream_t s) {
+  constexpr int CKMAX = K == 128 ? 32 : 64;
+  hipLaunchKernelGGL((bwd_reverse_kernel<K, VT, CKMAX>), dim3(B * H * p.nvt), dim3(256), 0, s, q, k, v, z, A_log,
+                     dt_bias, beta, scale, d_o, d_state_out, (const float*)ws, (float*)(ws + p.off_scratch),
+                     (float*)(ws + p.off_part), dv, dstate_in, H, T, V, p.CK, p.nck, p.nvt);
+  return hipGetLastError();
+}
+
+template <int K>
+static hipError_t launch_rev_k(const BwdPlan& p, const float* q, const float* k, const float* v, const float* z,
+                               const float* A_log, const float* dt_bias, const float* beta, float scale,
+                               const float* d_o, const float* d_state_out, char* ws, float* dv, float* dstate_in,
+                               int B, int H, int T, int V, hipStream_t s) {
+  switch (p.VT) {
+    case 8: return launch_rev<K, 8>(p, q, k, v, z, A_log, dt_bias, beta, scale, d_o, d_state_out, ws, dv, dstate_in, B, H, T, V, s);
+    case 16: return launch_rev<K, 16>(p, q, k, v, z, A_log, dt_bias, beta, scale, d_o, d_state_out, ws, dv, dstate_in, B, H, T, V, s);
+    default: return launch_rev<K, 32>(p, q, k, v, z, A_log, dt_bias, beta, scale, d_o, d_state_out, ws, dv, dstate_in, B, H, T, V, s);
+  }
+}
+
+hipError_t launch_chunk_bwd(const float* q, const float* k, const float* v, const float* z, const float* A_log,
+                            const float* dt_bias, const float* beta, const float* state_in, float scale, int chunk,
+                            const float* d_o, const float* d_state_out, float* dq, float* dk, float* dv, float* dg,
+                            float* dbeta, float* dstate_in, void* workspace, int B, int H, int T, int K, int V,
+                            hipStream_t s) {
+  BwdPlan p;
+  if (!bwd_plan(B, H, T, K, V, chunk, &p)) return hipErrorInvalidValue;
+  char* ws = static_cast<char*>(workspace);
+  hipError_t err = hipSuccess;
+  if (T > 0) {
+    switch (p.fwd.KD) {
+      case 16: err = launch_chunk_fwd_kd<float, 16>(p.fwd.VT, p.fwd.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, nullptr, nullptr, (float*)ws, B, H, T, K, V, s); break;
+      case 32: err = launch_chunk_fwd_kd<float, 32>(p.fwd.VT, p.fwd.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, nullptr, nullptr, (float*)ws, B, H, T, K, V, s); break;
+      case 64: err = launch_chunk_fwd_kd<float, 64>(p.fwd.VT, p.fwd.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, nullptr, nullptr, (float*)ws, B, H, T, K, V, s); break;
+      default: err = launch_chunk_fwd_kd<float, 128>(p.fwd.VT, p.fwd.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, nullptr, nullptr, (float*)ws, B, H, T, K, V, s); break;
+    }
+    if (err != hipSuccess) return err;
+  }
+  switch (K) {
+    case 8: err = launch_rev_k<8>(p, q, k, v, z, A_log, dt_bias, beta, scale, d_o, d_state_out, ws, dv, dstate_in, B, H, T, V, s); break;
+    case 16: err = launch_rev_k<16>(p, q, k, v, z, A_log, dt_bias, beta, scale, d_o, d_state_out, ws, dv, dstate_in, B, H, T, V, s); break;
+    case 32: err = launch_rev_k<32>(p, q, k, v, z, A_log, dt_bias, beta, scale, d_o, d_state_out, ws, dv, dstate_in, B, H, T, V, s); break;
+    case 64: err = launch_rev_k<64>(p, q, k, v, z, A_log, dt_bias, beta, scale, d_o, d_state_out, ws, dv, dstate_in, B, H, T, V, s); break;
+    default: err = launch_rev_k<128>(p, q, k, v, z, A_log, dt_bias, beta, scale, d_o, d_state_out, ws, dv, dstate_in, B, H, T, V, s); break;
+  }
+  if (err != hipSuccess) return err;
+  const long long BHT = (long long)B * H * T;
+  if (BHT > 0) {
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((BHT + 3) / 4)), dim3(256), 0, s,
+                       (const float*)(ws + p.off_part), k, dq, dk, dg, dbeta, BHT, K, p.nvt);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+}  // namespace kda

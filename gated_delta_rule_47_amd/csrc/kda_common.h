@@ -1,0 +1,110 @@
+// Device-side building blocks shared by the KDA kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef uint16_t bf16_t;   // bfloat16 bit pattern as stored in HBM and LDS
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short8 __attribute__((ext_vector_type(8)));
+typedef short short4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kALogMin = -10.0f;
+constexpr float kALogMax = 20.0f;
+
+// ------------------------------------------------------------------ conversions
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ bf16_t f2bf(float f) {   // round to nearest even (v_cvt_pk_bf16_f32)
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T x);
+template <> __device__ __forceinline__ float to_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t x) { return bf2f(x); }
+
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float x) { return f2bf(x); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// ------------------------------------------------------------------ gate
+// Multiplier exp(clamp(A_log, -10, 20)) of the released KDA gate (the clamp stays,
+// kdafix page "Fix 1 -- decay form").  Evaluated once per head with the precise expf.
+__device__ __forceinline__ float gate_multiplier(float a_log) {
+  return expf(fminf(fmaxf(a_log, kALogMin), kALogMax));
+}
+
+// softplus(x) = max(x,0) + log(1 + e^-|x|), natural units.  log1p is taken from the
+// hardware log2 of u = 1 + y; with `precise`, the rounding of u is undone by the
+// factor y / (u - 1) (Kahan's log1p identity), which keeps full relative accuracy
+// when y = e^-|x| is tiny.  That matters once the multiplier exp(A) is large.
+__device__ __forceinline__ float softplus_f(float x, bool precise) {
+  float y = fast_exp2(-fabsf(x) * kLog2e);
+  float u = 1.0f + y;
+  float l = fast_log2(u) * kLn2;
+  if (precise) {
+    float d = u - 1.0f;
+    l = (d == 0.0f) ? y : l * (y * fast_rcp(d));
+  }
+  return fmaxf(x, 0.0f) + l;
+}
+
+// ------------------------------------------------------------------ MFMA fragments
+// One wave computes a 16x16 fp32 tile C += A(16 x KS) * B(KS x 16) per instruction.
+// Operands live in LDS "depth-contiguous": A as [row][depth], B as [col][depth].
+// Lane l supplies row/col (l % 16) and depth elements starting at DPL*(l / 16).
+// The accumulator holds C[4*(l/16) + r][l % 16], r = 0..3.
+template <typename Top> struct Mfma;
+
+template <> struct Mfma<float> {            // v_mfma_f32_16x16x4_f32
+  static constexpr int KS = 4;
+  typedef float frag;
+  static __device__ __forceinline__ frag load(const float* base, int ld, int rc0, int k0, int lane) {
+    return base[(rc0 + (lane & 15)) * ld + k0 + (lane >> 4)];
+  }
+  static __device__ __forceinline__ floatx4 mma(frag a, frag b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  // multiply the depth elements of a fragment by per-depth factors f[k0 + ...]
+  static __device__ __forceinline__ frag scale(frag a, const float* f, int k0, int lane) {
+    return a * f[k0 + (lane >> 4)];
+  }
+};
+
+template <> struct Mfma<bf16_t> {           // v_mfma_f32_16x16x32_bf16
+  static constexpr int KS = 32;
+  typedef short8 frag;
+  static __device__ __forceinline__ frag load(const bf16_t* base, int ld, int rc0, int k0, int lane) {
+    return *reinterpret_cast<const short8*>(base + (rc0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+  }
+  static __device__ __forceinline__ floatx4 mma(frag a, frag b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag scale(frag a, const float* f, int k0, int lane) {
+    const float* fp = f + k0 + 8 * (lane >> 4);
+    frag r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (short)f2bf(bf2f((bf16_t)a[e]) * fp[e]);
+    return r;
+  }
+};
+
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+
+}  // namespace kda

@@ -1,0 +1,43 @@
+// Host-side launchers of the KDA kernels (definitions in the .hip files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "kda_common.h"
+
+namespace kda {
+
+template <typename Tin>
+hipError_t launch_gate(const void* z, const float* A_log, const float* dt_bias, float* g, float* alpha, int B, int H,
+                       int T, int K, hipStream_t s);
+
+template <typename Tin>
+hipError_t launch_step(const void* q, const void* k, const void* v, const void* z, const float* A_log,
+                       const float* dt_bias, const void* beta, float* state, float scale, void* o, int B, int H,
+                       int K, int V, hipStream_t s);
+
+// Chunked forward: instance chosen by (padded key dim KD, value tile VT, chunk C).
+// ckpt (nullable) receives the state at every chunk start: (B,H,ceil(T/C),K,V) fp32.
+template <typename Tin, int KD>
+hipError_t launch_chunk_fwd_kd(int VT, int C, const void* q, const void* k, const void* v, const void* z,
+                               const float* A_log, const float* dt_bias, const void* beta, const float* state_in,
+                               float scale, void* o, float* state_out, float* ckpt, int B, int H, int T, int K, int V,
+                               hipStream_t s);
+
+// Forward tiling actually used for (dtype, K, V, chunk): padded key dim, value tile
+// and the chunk the kernel blocks by.  Returns false when no instance exists.
+struct FwdPlan {
+  int KD, VT, C;
+};
+bool fwd_plan(bool bf16, int K, int V, int chunk, FwdPlan* plan);
+
+// Adjoint (fp32 activations).
+size_t bwd_workspace_bytes(int B, int H, int T, int K, int V, int chunk);
+hipError_t launch_chunk_bwd(const float* q, const float* k, const float* v, const float* z, const float* A_log,
+                            const float* dt_bias, const float* beta, const float* state_in, float scale, int chunk,
+                            const float* d_o, const float* d_state_out, float* dq, float* dk, float* dv, float* dg,
+                            float* dbeta, float* dstate_in, void* workspace, int B, int H, int T, int K, int V,
+                            hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,149 @@
+/*
+ * kda.h -- C ABI of libkda: Kimi Delta Attention (KDA) forward, decode step and
+ * adjoint on AMD Instinct MI355X (gfx950), hand-written HIP kernels.
+ *
+ * The method (per batch b, head h; sources are the burn-kda review pages):
+ *   gate     g = -exp(clamp(A_log[h], -10, 20)) * softplus(z + dt_bias[h,:])
+ *            alpha = exp(g)                      ("kdafix" page, "Fix 1 -- decay form":
+ *                                                 softplus first, the exp(A) multiplier outside)
+ *   scale    q_hat = scale * q, default scale = K^-0.5  ("kdafix" page, "Fix 2 -- read scale")
+ *   per token t (the gated delta rule):
+ *            S' = diag(alpha_t) S
+ *            S  = S' + beta_t k_t (v_t - S'^T k_t)^T
+ *            o_t = S^T q_hat_t
+ *   The chunked forward evaluates the same result in blocks of `chunk` tokens
+ *   (WY form; the carry decays by exp(G_last - G), "The fused KDA adjoint" page,
+ *   section 2).  Results equal the token recurrence up to floating-point rounding.
+ *
+ * Conventions shared by every entry point:
+ *   - Layout is head-major and contiguous: q, k, z, g: (B,H,T,K); v, o: (B,H,T,V);
+ *     beta: (B,H,T); state: (B,H,K,V) float32 (row = key channel, column = value
+ *     channel); A_log: (H) float32; dt_bias: (H,K) float32.
+ *   - `dtype` (KDA_F32 or KDA_BF16) is the element type of the activations q, k,
+ *     v, z, beta and of the output o.  States, A_log, dt_bias, g, alpha and all
+ *     gradients are float32 whatever `dtype` is.
+ *   - Every pointer is a device pointer.  The caller allocates and owns every
+ *     buffer; the library keeps nothing between calls and allocates nothing.
+ *     When T = 0, pointers to buffers with a T dimension may be NULL.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously on it; a call returns once its kernels are launched.
+ *   - Argument errors are reported before anything is launched, by a negative
+ *     status (kda_status below).  Nothing is printed, nothing is thrown across
+ *     the ABI, and there is no fallback path: an unsupported argument is an error.
+ *   - Supported sizes: K, V in {8, 16, 32, 64, 128}; chunk in {16, 32, 64};
+ *     B, H >= 1; T >= 0 (T = 0 writes nothing to o and copies state_in to
+ *     state_out).  T need not be a multiple of chunk: the last block behaves as
+ *     if padded with identity tokens (g = 0, beta = 0, q = k = v = 0), which leave
+ *     the state unchanged.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = -1,       /* a required pointer is NULL */
+  KDA_ERR_SHAPE = -2,      /* B, H, T, K or V out of range or unsupported */
+  KDA_ERR_DTYPE = -3,      /* unknown dtype, or a dtype this entry point does not take */
+  KDA_ERR_CHUNK = -4,      /* chunk not in {16, 32, 64} */
+  KDA_ERR_ALIAS = -5,      /* an output buffer aliases an input it must not alias */
+  KDA_ERR_HIP = -6,        /* a HIP launch or runtime call failed */
+  KDA_ERR_WORKSPACE = -7   /* workspace NULL or smaller than kda_chunk_bwd_workspace_bytes() */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* FLA's default read scale K^-0.5 as float ("kdafix" page, "Fix 2 -- read scale":
+ * every path folds it into q).  Returns 0 for K <= 0.  Host-only, no GPU work. */
+float kda_read_scale(int K);
+
+/* Fused decay gate ("kdafix" page, "Fix 1 -- decay form").
+ *   z        (B,H,T,K) in `dtype`
+ *   A_log    (H) float32, clamped to [-10, 20] before exp
+ *   dt_bias  (H,K) float32, may be NULL (= 0)
+ *   g_out    (B,H,T,K) float32: g <= 0
+ *   alpha_out (B,H,T,K) float32 = exp(g), may be NULL (not written)
+ * K may be any value >= 1 here.  g_out/alpha_out must not alias z. */
+int kda_gate(const void* z, const float* A_log, const float* dt_bias,
+             float* g_out, float* alpha_out,
+             int B, int H, int T, int K, int dtype, void* stream);
+
+/* Chunked KDA forward: the gate, the read-scale fold, the intra-chunk WY stage
+ * (decay-weighted strictly-lower beta k k^T, (I+A)^-1 by forward substitution,
+ * w and u), the inter-chunk state passing and the output, fused in one kernel.
+ *   q, k, z  (B,H,T,K) `dtype`;  v (B,H,T,V) `dtype`;  beta (B,H,T) `dtype`
+ *   A_log (H) f32;  dt_bias (H,K) f32 or NULL (= 0)
+ *   state_in  (B,H,K,V) f32, or NULL for a zero initial state
+ *   scale     read scale (pass kda_read_scale(K) for the default; 0 gives o = 0)
+ *   chunk     block size of the WY form, 16, 32 or 64.  For dtype KDA_F32 with
+ *             K = 128 the kernel blocks by min(chunk, 32) (on-chip memory); the
+ *             result is the same function.
+ *   o         (B,H,T,V) `dtype`; must not alias any input
+ *   state_out (B,H,K,V) f32 final state, or NULL (not written); may equal state_in
+ *             (each state tile is read before it is written by the same workgroup).
+ * Matrix products run on MFMA: bf16 operands with fp32 accumulation for
+ * KDA_BF16, fp32 operands for KDA_F32.  The state is carried in fp32. */
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* z,
+                  const float* A_log, const float* dt_bias, const void* beta,
+                  const float* state_in, float scale, int chunk,
+                  void* o, float* state_out,
+                  int B, int H, int T, int K, int V, int dtype, void* stream);
+
+/* One decode step of the same recurrence (the page's "decode prefill read" folds
+ * the scale into q the same way).  Inputs are one token per (b,h):
+ *   q, k, z (B,H,K) `dtype`;  v (B,H,V) `dtype`;  beta (B,H) `dtype`
+ *   state   (B,H,K,V) f32, read and updated in place
+ *   o       (B,H,V) `dtype`, must not alias an input
+ * Bound by the state's HBM traffic: 2*K*V*4 bytes per head and token. */
+int kda_recurrent_step(const void* q, const void* k, const void* v, const void* z,
+                       const float* A_log, const float* dt_bias, const void* beta,
+                       float* state, float scale, void* o,
+                       int B, int H, int K, int V, int dtype, void* stream);
+
+/* Bytes of device workspace kda_chunk_bwd needs for these sizes (0 on bad sizes). */
+size_t kda_chunk_bwd_workspace_bytes(int B, int H, int T, int K, int V, int chunk);
+
+/* Adjoint of the forward for L = sum(o * d_o) + sum(state_out * d_state_out)
+ * ("The fused KDA adjoint" page: the gradient blocks dq dk dv dg db dstate of its
+ * two-chunk fixture; the intra-chunk and the reverse inter-chunk recurrence).
+ * Inputs as kda_chunk_fwd, plus
+ *   d_o          (B,H,T,V) in `dtype`
+ *   d_state_out  (B,H,K,V) f32 or NULL (= 0)
+ * Outputs, all float32, none may alias an input:
+ *   dq, dk (B,H,T,K) w.r.t. the unscaled q and k;  dv (B,H,T,V);
+ *   dg (B,H,T,K) w.r.t. the log-decay g;  dbeta (B,H,T);  dstate_in (B,H,K,V).
+ * workspace: device buffer of at least kda_chunk_bwd_workspace_bytes(); its
+ * contents on entry are ignored.  Currently dtype must be KDA_F32. */
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z,
+                  const float* A_log, const float* dt_bias, const void* beta,
+                  const float* state_in, float scale, int chunk,
+                  const void* d_o, const float* d_state_out,
+                  float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dstate_in,
+                  void* workspace, size_t workspace_bytes,
+                  int B, int H, int T, int K, int V, int dtype, void* stream);
+
+/* Static string for a status code ("ok", "null pointer", ...). Never NULL. */
+const char* kda_status_string(int status);
+
+/* Copies up to n counters into out and returns how many exist (KDA_NUM_COUNTERS).
+ * Counters are process-wide and monotonic: calls accepted per entry point and
+ * calls rejected with an error status (modelled on the page's dispatch counters,
+ * "The fused KDA adjoint" page, section 6). */
+#define KDA_NUM_COUNTERS 5
+#define KDA_COUNTER_GATE 0
+#define KDA_COUNTER_CHUNK_FWD 1
+#define KDA_COUNTER_RECURRENT_STEP 2
+#define KDA_COUNTER_CHUNK_BWD 3
+#define KDA_COUNTER_REJECTED 4
+int kda_get_counters(unsigned long long* out, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -39,6 +39,14 @@ def algorithmic_bytes(wl) -> int:
     return acts + state + params
 
 
+def kernel_source_hash() -> str:
+    """sha256 of the fused forward kernel's source: counter-measured traffic is only
+    reported while the kernel it was measured on is unchanged."""
+    import hashlib
+    p = os.path.join(ROOT, "gated_delta_rule_47_amd", "csrc", "kda_chunk_fwd.h")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()
+
+
 def _oracle_head(args):
     """CPU baseline worker: the f64 oracle's token recurrence on one head."""
     wl_name, b, h = args
@@ -75,7 +83,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_long.json"),
                     help="HBM traffic per launch measured by rocprofv3 counters (if present)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of the benchmark, run a plain device-to-device copy of this many MiB "
+                         "(--steps times), to calibrate the FETCH_SIZE/WRITE_SIZE counters")
     args = ap.parse_args()
+    if args.copy_calibration_mib:
+        import torch
+        n = args.copy_calibration_mib * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": args.steps}))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (heads shard across GPUs "
               "with no communication; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
@@ -131,7 +152,7 @@ def main():
     if os.path.exists(args.traffic_json):
         try:
             tj = json.load(open(args.traffic_json))
-            if tj.get("workload") == wl.name:
+            if tj.get("workload") == wl.name and tj.get("kernel_source_sha256") == kernel_source_hash():
                 traffic = tj.get("bytes_per_launch")
         except Exception:
             traffic = None

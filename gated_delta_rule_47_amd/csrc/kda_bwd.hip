@@ -79,7 +79,7 @@ bwd_reverse_kernel(const float* __restrict__ q, const float* __restrict__ k, con
         sRed[parity][1][wave][4 * b + j] = p2[j];
       }
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float s0 = 0.0f, s1 = 0.0f;
@@ -94,7 +94,7 @@ bwd_reverse_kernel(const float* __restrict__ q, const float* __restrict__ k, con
   for (int ci = nck - 1; ci >= 0; --ci) {
     const int tc0 = ci * CK;
     const int n = min(CK, T - tc0);
-    __syncthreads();
+    lds_barrier();
     for (int idx = tid; idx < n * K; idx += 256) {
       const int t = idx / K, c = idx % K;
       const size_t g = ((size_t)bh * T + tc0 + t) * K + c;
@@ -116,7 +116,7 @@ bwd_reverse_kernel(const float* __restrict__ q, const float* __restrict__ k, con
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) S[i][j] = act ? ck[(size_t)(4 * a + i) * V + v0 + 4 * b + j] : 0.0f;
-    __syncthreads();
+    lds_barrier();
 
     // forward recompute: the states after tokens 0..n-2 of this chunk
     for (int t = 0; t < n - 1; ++t) {

@@ -74,7 +74,8 @@ struct FwdCfg {
   static constexpr int OFF_D0 = OFF_G0 + NB * KD * 4;
   static constexpr int OFF_F = OFF_D0 + NB * KD * 4;
   static constexpr int OFF_GC = OFF_F + NPAIR * KD * 4;
-  static constexpr int TOTAL = OFF_GC + KD * 4;
+  static constexpr int OFF_FLAG = OFF_GC + KD * 4;                  // per-wave flags
+  static constexpr int TOTAL = OFF_FLAG + 16;
   static_assert(TOTAL <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
   static_assert(KD % KS == 0 && KD % 16 == 0 && C % 16 == 0, "tile shape");
   static_assert((SZ_TK | SZ_KT | SZ_VT | SZ_TT | SZ_A | SZ_ST) % 16 == 0, "16-byte alignment");
@@ -147,6 +148,7 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
   float* sD0 = reinterpret_cast<float*>(smem + Cfg::OFF_D0);
   float* sF = reinterpret_cast<float*>(smem + Cfg::OFF_F);
   float* sGC = reinterpret_cast<float*>(smem + Cfg::OFF_GC);
+  int* sFlag = reinterpret_cast<int*>(smem + Cfg::OFF_FLAG);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -181,7 +183,7 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
         if (row0 + r < K && col < vcols) sacc[i][r] = state_in[((size_t)bh * K + row0 + r) * V + v0 + col];
     }
   }
-  __syncthreads();
+  lds_barrier();
   auto write_st = [&]() {
 #pragma unroll
     for (int i = 0; i < NSW; ++i) {
@@ -190,7 +192,36 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
     }
   };
   write_st();
-  __syncthreads();
+  lds_barrier();
+
+  // Register prefetch of one chunk's raw activations: every load is unconditional
+  // (token index clamped to T-1, masked after), so a chunk's loads issue as one batch.
+  const int kpairs = K / 2;
+  const bool has_k = tid < kpairs * NB;
+  const int kc2 = tid % kpairs, kb = tid / kpairs;
+  const bool has_v = tid < (VT / 2) * NB;
+  const int vc2 = tid % (VT / 2), vb = tid / (VT / 2);
+  const int vcol = min(2 * vc2, vcols - 2);     // in-bounds column for every lane
+  Pair<Tin> rk[16], rq[16], rz[16], rv[16];
+  float rbeta = 0.0f;
+  auto prefetch = [&](int tn) {
+    const size_t tb = (size_t)bh * T;
+    if (has_k) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const size_t a = (tb + min(tn + 16 * kb + t, T - 1)) * K + 2 * kc2;
+        rk[t] = Pair<Tin>::load(k + a);
+        rq[t] = Pair<Tin>::load(q + a);
+        rz[t] = Pair<Tin>::load(z + a);
+      }
+    }
+    if (has_v) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) rv[t] = Pair<Tin>::load(v + (tb + min(tn + 16 * vb + t, T - 1)) * V + v0 + vcol);
+    }
+    if (tid < C) rbeta = to_f<Tin>(beta[tb + min(tn + tid, T - 1)]);
+  };
+  if (T > 0) prefetch(0);
 
   const int nck = (T + C - 1) / C;
   for (int t0 = 0; t0 < T; t0 += C) {
@@ -211,59 +242,75 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
     }
 
     // ============================================================ E1
+    // Thread = (pair of key channels, 16-token block): the gate, the block-local
+    // decay scans and the decay-weighted operands, from the registers prefetched
+    // during the previous chunk.  Tokens past T are identity tokens (all zero).
     bool bad = false;
-    for (int item = tid; item < K * NB; item += 256) {
-      const int c = item % K, b = item / K;
-      const float dtb = dt_bias ? dt_bias[h * K + c] : 0.0f;
-      const size_t gb = (tokbase + 16 * b) * K + c;
-      float kf[8], qf[8], g2[8];
+    if (has_k) {
+      const int c = 2 * kc2, b = kb;
+      const float dtb0 = dt_bias ? dt_bias[h * K + c] : 0.0f;
+      const float dtb1 = dt_bias ? dt_bias[h * K + c + 1] : 0.0f;
+      float g0[8], g1[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const bool ok = 16 * b + t < nval;
-        kf[t] = ok ? to_f<Tin>(k[gb + (size_t)t * K]) : 0.0f;
-        qf[t] = ok ? to_f<Tin>(q[gb + (size_t)t * K]) : 0.0f;
-        g2[t] = ok ? -mult2 * softplus_f(to_f<Tin>(z[gb + (size_t)t * K]) + dtb, precise) : 0.0f;
+        g0[t] = ok ? -mult2 * softplus_f(rz[t].x() + dtb0, precise) : 0.0f;
+        g1[t] = ok ? -mult2 * softplus_f(rz[t].y() + dtb1, precise) : 0.0f;
       }
-      float acc = 0.0f;                       // first half: L = e^(sum_{t<m<=7} g) ^ -1 >= 1
+      float a0 = 0.0f, a1 = 0.0f;               // first half: L = e^-(sum_{t<m<=7} g) >= 1
 #pragma unroll
       for (int t = 7; t >= 0; --t) {
         const int i = 16 * b + t;
-        const float L = fast_exp2(-acc), R = fast_exp2(acc);
-        sKE[i * LD_TK + c] = from_f<Top>(kf[t] * L);
-        sQE[i * LD_TK + c] = from_f<Top>(qf[t] * L);
-        sKR[i * LD_TK + c] = from_f<Top>(kf[t] * R);
-        acc += g2[t];
+        const bool ok = i < nval;
+        const float kx = ok ? rk[t].x() : 0.0f, ky = ok ? rk[t].y() : 0.0f;
+        const float qx = ok ? rq[t].x() : 0.0f, qy = ok ? rq[t].y() : 0.0f;
+        const float L0 = fast_exp2(-a0), R0 = fast_exp2(a0), L1 = fast_exp2(-a1), R1 = fast_exp2(a1);
+        store2<Top>(sKE + i * LD_TK + c, kx * L0, ky * L1);
+        store2<Top>(sQE + i * LD_TK + c, qx * L0, qy * L1);
+        store2<Top>(sKR + i * LD_TK + c, kx * R0, ky * R1);
+        a0 += g0[t];
+        a1 += g1[t];
       }
-      const float h1 = acc;
-      acc = 0.0f;                             // second half: L = e^(sum_{8<=m<=t} g) <= 1
+      const float h10 = a0, h11 = a1;
+      a0 = 0.0f;
+      a1 = 0.0f;                                // second half: L = e^(sum_{8<=m<=t} g) <= 1
 #pragma unroll
       for (int t = 8; t < 16; ++t) {
         const int i = 16 * b + t;
         const bool ok = i < nval;
-        const float kv = ok ? to_f<Tin>(k[gb + (size_t)t * K]) : 0.0f;
-        const float qv = ok ? to_f<Tin>(q[gb + (size_t)t * K]) : 0.0f;
-        acc += ok ? -mult2 * softplus_f(to_f<Tin>(z[gb + (size_t)t * K]) + dtb, precise) : 0.0f;
-        const float L = fast_exp2(acc), R = fast_exp2(-acc);
-        sKE[i * LD_TK + c] = from_f<Top>(kv * L);
-        sQE[i * LD_TK + c] = from_f<Top>(qv * L);
-        sKR[i * LD_TK + c] = from_f<Top>(kv * R);
+        a0 += ok ? -mult2 * softplus_f(rz[t].x() + dtb0, precise) : 0.0f;
+        a1 += ok ? -mult2 * softplus_f(rz[t].y() + dtb1, precise) : 0.0f;
+        const float kx = ok ? rk[t].x() : 0.0f, ky = ok ? rk[t].y() : 0.0f;
+        const float qx = ok ? rq[t].x() : 0.0f, qy = ok ? rq[t].y() : 0.0f;
+        const float L0 = fast_exp2(a0), R0 = fast_exp2(-a0), L1 = fast_exp2(a1), R1 = fast_exp2(-a1);
+        store2<Top>(sKE + i * LD_TK + c, kx * L0, ky * L1);
+        store2<Top>(sQE + i * LD_TK + c, qx * L0, qy * L1);
+        store2<Top>(sKR + i * LD_TK + c, kx * R0, ky * R1);
       }
-      sH1[b * KD + c] = h1;
-      sH2[b * KD + c] = acc;
-      bad |= (h1 < -thresh) || (acc < -thresh);
+      sH1[b * KD + c] = h10;
+      sH1[b * KD + c + 1] = h11;
+      sH2[b * KD + c] = a0;
+      sH2[b * KD + c + 1] = a1;
+      bad = fminf(fminf(h10, h11), fminf(a0, a1)) < -thresh;
     }
-    for (int item = tid; item < VT * NB; item += 256) {      // V^T, 16 tokens per item
-      const int vv = item % VT, b = item / VT;
-      float vals[16];
+    if (has_v) {                                // V^T rows for two value columns
+      const int b = vb;
+      float va[16], vb_[16];
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        const int i = 16 * b + t;
-        vals[t] = (i < nval && vv < vcols) ? to_f<Tin>(v[(tokbase + i) * V + v0 + vv]) : 0.0f;
+        const bool ok = 16 * b + t < nval && 2 * vc2 < vcols;
+        va[t] = ok ? rv[t].x() : 0.0f;
+        vb_[t] = ok ? rv[t].y() : 0.0f;
       }
-      store16<Top>(sVT + vv * LD_CT + 16 * b, vals);
+      store16<Top>(sVT + (2 * vc2) * LD_CT + 16 * b, va);
+      store16<Top>(sVT + (2 * vc2 + 1) * LD_CT + 16 * b, vb_);
     }
-    if (tid < C) sBeta[tid] = tid < nval ? to_f<Tin>(beta[tokbase + tid]) : 0.0f;
-    const int slow = __syncthreads_or(bad);
+    if (tid < C) sBeta[tid] = tid < nval ? rbeta : 0.0f;
+    if (t0 + C < T) prefetch(t0 + C);           // next chunk's loads overlap this chunk's work
+    const unsigned long long ballot = __ballot(bad);
+    if (lane == 0) sFlag[wave] = ballot != 0ull;
+    lds_barrier();
+    const int slow = sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3];
 
     if (slow) {
       // ========================================================== token-by-token chunk
@@ -286,7 +333,7 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
         }
         for (int vv = tid; vv < VD; vv += 256) sVv[vv] = vv < vcols ? to_f<Tin>(v[tok * V + v0 + vv]) : 0.0f;
         const float bt = to_f<Tin>(beta[tok]);
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int j = 0; j < NSW; ++j) {        // S' = diag(alpha) S; partial S'^T k
           const int tau = wave + 4 * j;
@@ -300,7 +347,7 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
             if (lane < 16) sRed[tau * 16 + l16] = pr;
           }
         }
-        __syncthreads();
+        lds_barrier();
         float po[NSW];
 #pragma unroll
         for (int j = 0; j < NSW; ++j) {        // S += beta k (v - r)^T; partial S^T q_hat
@@ -319,23 +366,23 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
             po[j] = pq;
           }
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int j = 0; j < NSW; ++j) {
           const int tau = wave + 4 * j;
           if (tau < NS && lane < 16) sRed[tau * 16 + l16] = po[j];
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < vcols && o) {
           const int nt = tid / 16;
           float ov = 0.0f;
           for (int mt = 0; mt < NMT; ++mt) ov += sRed[(mt * NNT + nt) * 16 + (tid & 15)];
           o[tok * V + v0 + tid] = from_f<Tin>(ov);
         }
-        __syncthreads();
+        lds_barrier();
       }
       write_st();
-      __syncthreads();
+      lds_barrier();
       continue;
     }
 
@@ -365,7 +412,7 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
           sF[pair_index(I, J) * KD + c] = fast_exp2(ex);
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ============================================================ E2a + AP
     for (int item = tid; item < K * NB; item += 256) {
@@ -416,7 +463,7 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ============================================================ E2b + diagonal inverses
     for (int item = tid; item < K * NB; item += 256) {
@@ -442,7 +489,7 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
 #pragma unroll
       for (int i = 0; i < 16; ++i) sA[(16 * I + i) * LD_A + 16 * I + j] = tcol[i];
     }
-    __syncthreads();
+    lds_barrier();
 
     // ============================================================ off-diagonal T blocks
 #pragma unroll
@@ -459,7 +506,7 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
 #pragma unroll
         for (int r = 0; r < 4; ++r) X[(4 * lg + r) * 16 + l16] = acc[r];
       }
-      __syncthreads();
+      lds_barrier();
       if (wave < I) {                          // T_IJ = -T_II X_J
         const int J = wave;
         const float* X = sX + wave * 256;
@@ -470,13 +517,13 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
 #pragma unroll
         for (int r = 0; r < 4; ++r) sA[(16 * I + 4 * lg + r) * LD_A + 16 * J + l16] = -acc[r];
       }
-      __syncthreads();
+      lds_barrier();
     }
     for (int idx = tid; idx < CD * CD; idx += 256) {      // T diag(beta)
       const int i = idx / CD, j = idx % CD;
       sTb[i * LD_CT + j] = from_f<Top>(sA[i * LD_A + j] * sBeta[j]);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ============================================================ W: -w = -(T diag(beta)) W~
     {
@@ -491,7 +538,7 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
         for (int r = 0; r < 4; ++r) sW[(16 * I + 4 * lg + r) * LD_TK + 16 * n + l16] = from_f<Top>(-acc[r]);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ============================================================ U = T diag(beta) V - w S   (stored as U^T)
     for (int task = wave; task < NBD * NNT; task += 4) {
@@ -507,7 +554,7 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
       }
       store4<Top>(sUT + (16 * n + l16) * LD_CT + 16 * I + 4 * lg, acc, 1.0f);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ============================================================ O and the state update
     for (int task = wave; task < NB * NNT; task += 4) {
@@ -541,9 +588,9 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
                             sacc[i]);
       }
     }
-    __syncthreads();
+    lds_barrier();
     write_st();
-    __syncthreads();
+    lds_barrier();
   }
 
   if (state_out) {

@@ -103,6 +103,49 @@ template <> struct Mfma<bf16_t> {           // v_mfma_f32_16x16x32_bf16
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
+// Workgroup barrier ordering LDS only.  The kernels never exchange data between
+// threads through global memory, so the barrier need not wait for outstanding
+// HBM loads and stores (a plain __syncthreads() fences global memory as well and
+// would stall every barrier on in-flight output stores and prefetches).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Two consecutive activation elements loaded with one 4-byte (bf16) or 8-byte
+// (fp32) access.
+template <typename T> struct Pair;
+template <> struct Pair<bf16_t> {
+  uint32_t u;
+  static __device__ __forceinline__ Pair load(const bf16_t* p) {
+    Pair r;
+    r.u = *reinterpret_cast<const uint32_t*>(p);
+    return r;
+  }
+  __device__ __forceinline__ float x() const { return __uint_as_float(u << 16); }
+  __device__ __forceinline__ float y() const { return __uint_as_float(u & 0xffff0000u); }
+};
+template <> struct Pair<float> {
+  float2 f;
+  static __device__ __forceinline__ Pair load(const float* p) {
+    Pair r;
+    r.f = *reinterpret_cast<const float2*>(p);
+    return r;
+  }
+  __device__ __forceinline__ float x() const { return f.x; }
+  __device__ __forceinline__ float y() const { return f.y; }
+};
+
+// Store two consecutive operand values.
+template <typename T> __device__ __forceinline__ void store2(T* dst, float a, float b);
+template <> __device__ __forceinline__ void store2<float>(float* dst, float a, float b) {
+  *reinterpret_cast<float2*>(dst) = float2{a, b};
+}
+template <> __device__ __forceinline__ void store2<bf16_t>(bf16_t* dst, float a, float b) {
+  *reinterpret_cast<uint32_t*>(dst) = (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
 constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 constexpr int cmin(int a, int b) { return a < b ? a : b; }

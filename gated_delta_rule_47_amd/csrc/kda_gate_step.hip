@@ -58,7 +58,7 @@ __global__ void __launch_bounds__(256) step_kernel(const Tin* __restrict__ q, co
     sK[c] = to_f<Tin>(k[(size_t)bh * K + c]);
     sQ[c] = scale * to_f<Tin>(q[(size_t)bh * K + c]);
   }
-  __syncthreads();
+  lds_barrier();
 
   float* S = state + (size_t)bh * K * V + v0 + vc;
   float s[RPT];
@@ -70,7 +70,7 @@ __global__ void __launch_bounds__(256) step_kernel(const Tin* __restrict__ q, co
     r += s[i] * sK[c];                         // partial S'^T k
   }
   sRed[rg * VTS + vc] = r;
-  __syncthreads();
+  lds_barrier();
   float rt = 0.0f;
 #pragma unroll
   for (int g = 0; g < NRG; ++g) rt += sRed[g * VTS + vc];
@@ -84,9 +84,9 @@ __global__ void __launch_bounds__(256) step_kernel(const Tin* __restrict__ q, co
     ov += s[i] * sQ[c];                        // partial S^T q_hat
     S[(size_t)c * V] = s[i];
   }
-  __syncthreads();
+  lds_barrier();
   sRed[rg * VTS + vc] = ov;
-  __syncthreads();
+  lds_barrier();
   if (rg == 0) {
     float ot = 0.0f;
 #pragma unroll

@@ -32,7 +32,7 @@ bool fwd_plan(bool bf16, int K, int V, int chunk, FwdPlan* p) {
   if (bf16) {
     p->KD = K < 32 ? 32 : K;
     p->VT = V < 16 ? 16 : (V > 64 ? 64 : V);
-    p->C = chunk;
+    p->C = chunk > 32 ? 32 : chunk;
   } else {
     p->KD = K < 16 ? 16 : K;
     const int vtmax = p->KD >= 64 ? 32 : 64;
@@ -49,11 +49,14 @@ static hipError_t launch_fwd(bool bf16, const FwdPlan& p, const void* q, const v
 #define KDA_FWD(TYPE, KD_)                                                                                    \
   return launch_chunk_fwd_kd<TYPE, KD_>(p.VT, p.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, o,     \
                                          state_out, nullptr, B, H, T, K, V, s)
+#define KDA_FWD_PC(KD_)                                                                                       \
+  return launch_chunk_fwd_pc_kd<KD_>(p.VT, p.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, o, state_out, B, \
+                                     H, T, K, V, s)
   if (bf16) {
     switch (p.KD) {
-      case 32: KDA_FWD(bf16_t, 32);
-      case 64: KDA_FWD(bf16_t, 64);
-      case 128: KDA_FWD(bf16_t, 128);
+      case 32: KDA_FWD_PC(32);
+      case 64: KDA_FWD_PC(64);
+      case 128: KDA_FWD_PC(128);
     }
   } else {
     switch (p.KD) {
@@ -64,6 +67,7 @@ static hipError_t launch_fwd(bool bf16, const FwdPlan& p, const void* q, const v
     }
   }
 #undef KDA_FWD
+#undef KDA_FWD_PC
   return hipErrorInvalidValue;
 }
 
@@ -91,6 +95,7 @@ const char* kda_status_string(int status) {
     case KDA_ERR_ALIAS: return "output aliases an input";
     case KDA_ERR_HIP: return "HIP launch or runtime error";
     case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_ALIGN: return "misaligned activation pointer";
     default: return "unknown status";
   }
 }
@@ -127,6 +132,11 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* z, co
   if (B < 1 || H < 1 || T < 0 || !valid_dim(K) || !valid_dim(V)) return reject(KDA_ERR_SHAPE);
   if (!valid_chunk(chunk)) return reject(KDA_ERR_CHUNK);
   const size_t es = esize(dtype);
+  // one head's activations are addressed with 32-bit byte offsets (including the
+  // reads of up to 64 tokens past T that the range check turns into zeros)
+  if ((size_t)(T + 64) * (size_t)(K > V ? K : V) * es > 0x7fffffffu) return reject(KDA_ERR_SHAPE);
+  const uintptr_t amask = 2 * es - 1;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)z) & amask) return reject(KDA_ERR_ALIGN);
   const size_t nk = (size_t)B * H * T * K * es, nv = (size_t)B * H * T * V * es, nb = (size_t)B * H * T * es;
   const size_t ns = (size_t)B * H * K * V * 4;
   const void* ins[] = {q, k, z};
@@ -197,6 +207,8 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z, co
   if (dtype != KDA_F32) return reject(KDA_ERR_DTYPE);
   if (B < 1 || H < 1 || T < 0 || !valid_dim(K) || !valid_dim(V)) return reject(KDA_ERR_SHAPE);
   if (!valid_chunk(chunk)) return reject(KDA_ERR_CHUNK);
+  if ((size_t)(T + 64) * (size_t)(K > V ? K : V) * 4 > 0x7fffffffu) return reject(KDA_ERR_SHAPE);
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)z) & 7) return reject(KDA_ERR_ALIGN);
   const size_t need = bwd_workspace_bytes(B, H, T, K, V, chunk);
   if (!workspace || workspace_bytes < need) return reject(KDA_ERR_WORKSPACE);
   const size_t nk = (size_t)B * H * T * K * 4, nv = (size_t)B * H * T * V * 4, nb = (size_t)B * H * T * 4;

@@ -137,13 +137,30 @@ template <> struct Pair<float> {
   __device__ __forceinline__ float y() const { return f.y; }
 };
 
+// Buffer resource over [base, base + bytes): 32-bit byte offsets, and the hardware
+// range check returns 0 for any load past the end (raw buffer, 32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint32_t buf_load_b32(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+// Two floats rounded to bf16 and packed low/high in one register (one v_cvt_pk_bf16_f32:
+// a two-element vector conversion, so the pair is never split into scalar conversions).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){a, b}, bf16x2_t));
+}
+
 // Store two consecutive operand values.
 template <typename T> __device__ __forceinline__ void store2(T* dst, float a, float b);
 template <> __device__ __forceinline__ void store2<float>(float* dst, float a, float b) {
   *reinterpret_cast<float2*>(dst) = float2{a, b};
 }
 template <> __device__ __forceinline__ void store2<bf16_t>(bf16_t* dst, float a, float b) {
-  *reinterpret_cast<uint32_t*>(dst) = (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(a, b);
 }
 
 constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }

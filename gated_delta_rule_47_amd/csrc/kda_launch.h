@@ -25,6 +25,13 @@ hipError_t launch_chunk_fwd_kd(int VT, int C, const void* q, const void* k, cons
                                float scale, void* o, float* state_out, float* ckpt, int B, int H, int T, int K, int V,
                                hipStream_t s);
 
+// Pipelined bf16 forward (8 waves, internal blocks of C <= 32 tokens).
+template <int KD>
+hipError_t launch_chunk_fwd_pc_kd(int VT, int C, const void* q, const void* k, const void* v, const void* z,
+                                  const float* A_log, const float* dt_bias, const void* beta, const float* state_in,
+                                  float scale, void* o, float* state_out, int B, int H, int T, int K, int V,
+                                  hipStream_t s);
+
 // Forward tiling actually used for (dtype, K, V, chunk): padded key dim, value tile
 // and the chunk the kernel blocks by.  Returns false when no instance exists.
 struct FwdPlan {

@@ -53,7 +53,8 @@ typedef enum {
   KDA_ERR_CHUNK = -4,      /* chunk not in {16, 32, 64} */
   KDA_ERR_ALIAS = -5,      /* an output buffer aliases an input it must not alias */
   KDA_ERR_HIP = -6,        /* a HIP launch or runtime call failed */
-  KDA_ERR_WORKSPACE = -7   /* workspace NULL or smaller than kda_chunk_bwd_workspace_bytes() */
+  KDA_ERR_WORKSPACE = -7,  /* workspace NULL or smaller than kda_chunk_bwd_workspace_bytes() */
+  KDA_ERR_ALIGN = -8       /* an activation pointer is not aligned to two elements */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -80,9 +81,14 @@ int kda_gate(const void* z, const float* A_log, const float* dt_bias,
  *   A_log (H) f32;  dt_bias (H,K) f32 or NULL (= 0)
  *   state_in  (B,H,K,V) f32, or NULL for a zero initial state
  *   scale     read scale (pass kda_read_scale(K) for the default; 0 gives o = 0)
- *   chunk     block size of the WY form, 16, 32 or 64.  For dtype KDA_F32 with
- *             K = 128 the kernel blocks by min(chunk, 32) (on-chip memory); the
- *             result is the same function.
+ *   chunk     block size of the WY form, 16, 32 or 64.  The kernels block by at
+ *             most 32 tokens where on-chip memory or registers require it (every
+ *             KDA_BF16 call; KDA_F32 with K = 128); the result is the same function.
+ *   q, k, v, z must be aligned to two elements (4 bytes for KDA_BF16, 8 for
+ *   KDA_F32): the kernels load channel pairs (KDA_ERR_ALIGN otherwise).  One
+ *   head's sequence must span less than 2 GiB: (T + 64) * max(K, V) * element
+ *   size < 2^31, since the kernels address it with 32-bit offsets (KDA_ERR_SHAPE
+ *   otherwise).
  *   o         (B,H,T,V) `dtype`; must not alias any input
  *   state_out (B,H,K,V) f32 final state, or NULL (not written); may equal state_in
  *             (each state tile is read before it is written by the same workgroup).

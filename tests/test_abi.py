@@ -46,8 +46,8 @@ def test_read_scale():
 def test_status_strings_and_counters():
     lib = _lib()
     assert lib.kda_status_string(0) == b"ok"
-    names = {lib.kda_status_string(s) for s in range(-7, 1)}
-    assert len(names) == 8 and b"unknown status" not in names
+    names = {lib.kda_status_string(s) for s in range(-8, 1)}
+    assert len(names) == 9 and b"unknown status" not in names
     assert lib.kda_status_string(-99) == b"unknown status"
     n = lib.kda_get_counters(None, 0)
     arr = (ctypes.c_ulonglong * n)()
@@ -86,8 +86,16 @@ def test_argument_errors_before_launch():
     assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 12, 8, 0, None) == -2
     assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, 0, 1, 16, 8, 8, 0, None) == -2
     assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, -1, 8, 8, 0, None) == -2
+    # one head's sequence too long for 32-bit offsets (2^31 / (128 * 2) tokens, bf16)
+    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 1 << 23, 128, 128, 1,
+                             None) == -2
     # bad chunk
     assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 48, o, s_out, 1, 1, 16, 8, 8, 0, None) == -4
+    # activation pointer not aligned to two elements
+    assert lib.kda_chunk_fwd(q, P(0x20002), v, z, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 8, 1,
+                             None) == -8
+    assert lib.kda_chunk_fwd(q, k, v, P(0x40004), A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 8, 0,
+                             None) == -8
     # output aliasing an input
     assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, q, s_out, 1, 1, 16, 8, 8, 0, None) == -5
     assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, k, 1, 1, 16, 8, 8, 0, None) == -5
@@ -106,4 +114,4 @@ def test_argument_errors_before_launch():
     assert lib.kda_chunk_bwd(*args, g[0], 16, 1, 1, 16, 8, 8, 0, None) == -7
     rej1 = (ctypes.c_ulonglong * 5)()
     lib.kda_get_counters(rej1, 5)
-    assert rej1[4] - rej0[4] == 16 and list(rej1[:4]) == list(rej0[:4])
+    assert rej1[4] - rej0[4] == 19 and list(rej1[:4]) == list(rej0[:4])

@@ -3,17 +3,21 @@
 // One workgroup of 8 waves owns one (batch, head, value tile of <= 64 columns) and
 // walks the sequence in blocks of C <= 32 tokens.  The work of a block splits into
 //   K-side: the gate and block-local decay scans, the decay-weighted operands, the
-//           strictly-lower A and the lower P (MFMA), T = (I + A)^-1;
-//   V-side: Y = V - W~ S, U = T diag(beta) Y, o = scale (QGamma S + P U),
-//           S = diag(Gamma_C) S + KD^T U.
-// (U = T diag(beta) (V - W~ S) is the u - w S of the WY form with the product w = T
-// diag(beta) W~ folded into the state-dependent side, which removes one token x
-// channel product from the serial part of the walk.)  Only the V-side depends on the
-// state.  Each step of the walk runs
+//           strictly-lower A and the lower P (MFMA), the inverses T_00, T_11 of the two
+//           16x16 diagonal blocks of I + A;
+//   V-side: with S~ = diag(G0) S,  Y = V - KE S~,  U = (I + A)^-1 diag(beta) Y,
+//           o = scale (QE S~ + P U),  S = diag(D0) (S~ + KR^T U).
+// (U = (I + A)^-1 diag(beta) (V - W~ S) is the u - w S of the WY form with the product
+// w = T diag(beta) W~ folded into the state-dependent side, which removes one token x
+// channel product from the serial part of the walk.  The V-side applies the inverse
+// blockwise, U_0 = T_00 Z_0 and U_1 = T_11 (Z_1 - A_10 U_0) with Z = diag(beta) Y, so
+// the off-diagonal block of the inverse is never formed.)  Only the V-side depends on
+// the state.  Each step of the walk runs
 //   phase 1: waves 0-3 compute the gate/scan/operands of block c+1 (VALU) while waves
 //            4-7 run the V-side of block c (MFMA), each owning 16 value columns and all
 //            K rows of the fp32 state in accumulator registers;
-//   phase 2: the A/P tiles (7 waves), then T (wave 0), for block c+1.
+//   phase 2: the A/P tiles (7 waves), then T_00 (wave 0) and T_11 (wave 1), for
+//            block c+1.
 // Operands written in phase 1 and read by the V-side are double-buffered in LDS.
 //
 // Activations reach LDS by buffer-to-LDS DMA (16 bytes per lane, 1 KB per instruction),
@@ -31,10 +35,15 @@
 // serve as A or as B operand, so a product can be computed transposed when that makes
 // its result layout the one the next step (or the global store) wants.
 //
-// Decay factors follow the block-midpoint factorisation of the single-wave-group kernel
-// (kda_chunk_fwd.h): every L, R, Gamma0, D0 and F factor is 2^x with |x| bounded by one
-// half-block of decay; a block whose half-block decay exceeds 2^thresh is evaluated
-// token by token by the V-side waves instead.
+// Decays are taken relative to one reference per 32-token block, the cumulative
+// log-decay m through its 16th token: KE = k 2^(G - m), QE = q 2^(G - m), KR = k 2^(m - G)
+// (G the cumulative log2-decay of each token), so A = KE KR^T and P = QE KR^T hold the
+// exact pairwise decays, and the chunk-level factors G0 = 2^m (block start to the
+// reference) and D0 = 2^(G_last - m) (reference to block end) are per-channel scalings
+// of the state: QGamma S = QE (G0 S), W~ S = KE (G0 S), and the carry
+// diag(Gamma_C) S + KD^T U = diag(D0) (G0 S + KR^T U) since Gamma_C = G0 D0.  Every factor
+// is 2^x with |x| at most one 16-token half of the block's decay; a block where that
+// exceeds 2^thresh in some channel is evaluated token by token by the V-side waves.
 #pragma once
 
 #include <type_traits>
@@ -51,8 +60,11 @@ struct PcCfg {
   static constexpr int VD = round_up(VT, 16);
   static constexpr int NNT = VD / 16;                 // value-column tiles = active V-side waves
   static constexpr int NMT = KD / 16;                 // key-row tiles of the state
-  static constexpr int LD_TK = KD + 8;                // [token][channel] bf16
-  static constexpr int LD_CT = CD + 8;                // [channel|token][token] bf16
+  // Row strides of the bf16 operand tiles, in elements: 2 (mod 32) banks of 4 bytes per
+  // row, so that the 8-byte operand reads (16 consecutive rows per 128-byte LDS cycle)
+  // and the 4-byte K-side writes (rows 8 apart) are free of bank conflicts.
+  static constexpr int LD_TK = KD + 4;                // [token][channel] bf16
+  static constexpr int LD_CT = CD + 4;                // [channel|token][token] bf16
   static constexpr int LD_A = CD + 4;                 // [token][token] fp32
   static constexpr int SZ_TK = CD * LD_TK * 2;
   static constexpr int SZ_KT = KD * LD_CT * 2;
@@ -63,23 +75,21 @@ struct PcCfg {
   static constexpr int QKZ_DMA = C * KD / 512;        // 1 KB DMA instructions per tensor and block
   static constexpr int VRAW_BUF = NNT * 1024;         // per value tile: 32 rows x 16 columns
   // working buffers (written in phase 1 for block c+1, read in phase 2)
-  static constexpr int OFF_KE = 0;
-  static constexpr int OFF_QE = OFF_KE + SZ_TK;
-  static constexpr int OFF_KR = OFF_QE + SZ_TK;
-  static constexpr int OFF_KRF = OFF_KR + SZ_TK;      // F_10 * KR of tokens 0..15
-  static constexpr int OFF_A = OFF_KRF + 16 * LD_TK * 2;   // A, then T (fp32)
-  static constexpr int OFF_X = OFF_A + CD * LD_A * 4; // 16x16 fp32 scratch
+  static constexpr int OFF_KR = 0;
+  static constexpr int OFF_A = OFF_KR + SZ_TK;        // diagonal blocks of A (fp32)
   // phase-2 outputs, read by the V-side in the next phase 1
-  static constexpr int OFF_P = OFF_X + 256 * 4;
-  static constexpr int OFF_T = OFF_P + SZ_TT;
-  // phase-1 outputs, double-buffered: -W~, QGamma, KD^T, Gamma_C, beta
-  static constexpr int SET_WN = 0;
-  static constexpr int SET_QG = SET_WN + SZ_TK;
-  static constexpr int SET_KDT = SET_QG + SZ_TK;
-  static constexpr int SET_GC = SET_KDT + SZ_KT;
-  static constexpr int SET_BETA = SET_GC + KD * 4;
+  static constexpr int OFF_P = OFF_A + CD * LD_A * 4;
+  static constexpr int OFF_T = OFF_P + SZ_TT;         // T_00 and T_11, zero elsewhere
+  static constexpr int OFF_A10 = OFF_T + SZ_TT;       // -A_10 in columns 0..15, zero in 16..31
+  // phase-1 outputs, double-buffered: KE, QE, KR^T, G0, D0, beta
+  static constexpr int SET_KE = 0;
+  static constexpr int SET_QE = SET_KE + SZ_TK;
+  static constexpr int SET_KRT = SET_QE + SZ_TK;
+  static constexpr int SET_G0 = SET_KRT + SZ_KT;
+  static constexpr int SET_D0 = SET_G0 + KD * 4;
+  static constexpr int SET_BETA = SET_D0 + KD * 4;
   static constexpr int SET_BYTES = SET_BETA + CD * 4;
-  static constexpr int OFF_SET = OFF_T + SZ_TT;
+  static constexpr int OFF_SET = OFF_A10 + 16 * LD_CT * 2;
   static constexpr int OFF_RAW = OFF_SET + 2 * SET_BYTES;
   static constexpr int OFF_VRAW = OFF_RAW + 2 * RAW_BUF;
   static constexpr int OFF_FLAG = OFF_VRAW + 2 * VRAW_BUF;
@@ -112,10 +122,6 @@ __device__ __forceinline__ short8 acc_perm(floatx4 x0, floatx4 x1) {
 __device__ __forceinline__ floatx4 mfma_bf16(short8 a, short8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                  0, 0);
-}
-
-__device__ __forceinline__ short8 lds_frag(const bf16_t* base, int ld, int rc0, int k0, int lane) {
-  return *reinterpret_cast<const short8*>(base + (rc0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
 }
 
 __device__ __forceinline__ void store4_bf16(bf16_t* dst, float a, float b, float c, float d) {
@@ -161,12 +167,9 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   constexpr int NS = KD / 32;                         // 32-deep channel slices
 
   __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
-  bf16_t* sKE = reinterpret_cast<bf16_t*>(smem + Cfg::OFF_KE);
-  bf16_t* sQE = reinterpret_cast<bf16_t*>(smem + Cfg::OFF_QE);
   bf16_t* sKR = reinterpret_cast<bf16_t*>(smem + Cfg::OFF_KR);
-  bf16_t* sKRF = reinterpret_cast<bf16_t*>(smem + Cfg::OFF_KRF);
   float* sA = reinterpret_cast<float*>(smem + Cfg::OFF_A);
-  float* sX = reinterpret_cast<float*>(smem + Cfg::OFF_X);
+  bf16_t* sA10 = reinterpret_cast<bf16_t*>(smem + Cfg::OFF_A10);
   bf16_t* sP = reinterpret_cast<bf16_t*>(smem + Cfg::OFF_P);
   bf16_t* sT = reinterpret_cast<bf16_t*>(smem + Cfg::OFF_T);
   int* sFlag = reinterpret_cast<int*>(smem + Cfg::OFF_FLAG);   // [set][wave]
@@ -244,10 +247,11 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     constexpr bool PRECISE = decltype(precise_tag)::value;
     const int nval = min(C, T - tn);
     char* sb = set_base(set);
-    bf16_t* sWN = reinterpret_cast<bf16_t*>(sb + Cfg::SET_WN);
-    bf16_t* sQG = reinterpret_cast<bf16_t*>(sb + Cfg::SET_QG);
-    bf16_t* sKDT = reinterpret_cast<bf16_t*>(sb + Cfg::SET_KDT);
-    float* sGC = reinterpret_cast<float*>(sb + Cfg::SET_GC);
+    bf16_t* sKE = reinterpret_cast<bf16_t*>(sb + Cfg::SET_KE);
+    bf16_t* sQE = reinterpret_cast<bf16_t*>(sb + Cfg::SET_QE);
+    bf16_t* sKRT = reinterpret_cast<bf16_t*>(sb + Cfg::SET_KRT);
+    float* sG0 = reinterpret_cast<float*>(sb + Cfg::SET_G0);
+    float* sD0 = reinterpret_cast<float*>(sb + Cfg::SET_D0);
     float* sBeta = reinterpret_cast<float*>(sb + Cfg::SET_BETA);
     // raw k, q, z of channel pair `pair`, tokens 8hb..8hb+7 (staging buffer of this block)
     Pair<bf16_t> rk[8], rq[8], rz[8];
@@ -264,31 +268,20 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
 #pragma unroll
       for (int t = 0; t < 8; ++t) rk[t].u = rq[t].u = rz[t].u = 0u;
     }
-    // gate in log2 units, for every staged token (rows past T hold 0: finite)
-    float gx[8], gy[8];
+    // Tokens at or past nval (a partial last block, or rows 16..31 when C = 16) are
+    // identity tokens: their staged k and q are 0, and z = -inf makes their gate 0.
+    if (nval < CD) {
+      const int lim = nval - 8 * hb;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      gx[t] = -mult2 * softplus_f(rz[t].x() + dtb0, PRECISE);
-      gy[t] = -mult2 * softplus_f(rz[t].y() + dtb1, PRECISE);
+      for (int t = 0; t < 8; ++t) rz[t].u = t < lim ? rz[t].u : 0xFF80FF80u;
     }
-    if (nval < CD) {                       // wave-uniform: a partial block, or C = 16
-      const int lim = nval - 8 * hb;       // tokens at or past nval act as identity tokens
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const bool ok = t < lim;
-        gx[t] = ok ? gx[t] : 0.0f;
-        gy[t] = ok ? gy[t] : 0.0f;
-        rk[t].u = ok ? rk[t].u : 0u;
-        rq[t].u = ok ? rq[t].u : 0u;
-      }
-    }
-    // inclusive prefix over the lane's 8 tokens
+    // gate in log2 units and its inclusive prefix over the lane's 8 tokens
     float px[8], py[8];
     float ax = 0.0f, ay = 0.0f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      ax += gx[t];
-      ay += gy[t];
+      ax += -mult2 * softplus_f(rz[t].x() + dtb0, PRECISE);
+      ay += -mult2 * softplus_f(rz[t].y() + dtb1, PRECISE);
       px[t] = ax;
       py[t] = ay;
     }
@@ -296,44 +289,38 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     float Hx[4], Hy[4];
     row_gather(ax, Hx);
     row_gather(ay, Hy);
-    const int b = hb >> 1;
-    const bool first = (hb & 1) == 0;
-    const float G0x = fast_exp2(b ? Hx[0] + Hx[1] + Hx[2] : Hx[0]);   // chunk start -> block midpoint
-    const float G0y = fast_exp2(b ? Hy[0] + Hy[1] + Hy[2] : Hy[0]);
-    const float D0x = fast_exp2(b ? Hx[3] : Hx[1] + Hx[2] + Hx[3]);   // block midpoint -> chunk end
-    const float D0y = fast_exp2(b ? Hy[3] : Hy[1] + Hy[2] + Hy[3]);
-    const float F0x = fast_exp2(Hx[1] + Hx[2]), F0y = fast_exp2(Hy[1] + Hy[2]);   // midpoint 0 -> midpoint 1
+    // exponent of token t relative to the reference m = H0 + H1: G_t - m
+    const float offx = hb == 0 ? -(Hx[0] + Hx[1]) : hb == 1 ? -Hx[1] : hb == 2 ? 0.0f : Hx[2];
+    const float offy = hb == 0 ? -(Hy[0] + Hy[1]) : hb == 1 ? -Hy[1] : hb == 2 ? 0.0f : Hy[2];
     if (kact) {
       const int c = 2 * pair;
-      float kdx[8], kdy[8];
+      float krx[8], kry[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const float ex = first ? px[t] - ax : px[t], ey = first ? py[t] - ay : py[t];
+        const float ex = px[t] + offx, ey = py[t] + offy;
         const float Lx = fast_exp2(ex), Ly = fast_exp2(ey), Rx = fast_exp2(-ex), Ry = fast_exp2(-ey);
         const float kx = rk[t].x(), ky = rk[t].y(), qx = rq[t].x(), qy = rq[t].y();
         const int j = 8 * hb + t;
-        const float kex = kx * Lx, key = ky * Ly, qex = qx * Lx, qey = qy * Ly, krx = kx * Rx, kry = ky * Ry;
-        store2<bf16_t>(sKE + j * LD_TK + c, kex, key);
-        store2<bf16_t>(sQE + j * LD_TK + c, qex, qey);
-        store2<bf16_t>(sKR + j * LD_TK + c, krx, kry);
-        store2<bf16_t>(sQG + j * LD_TK + c, qex * G0x, qey * G0y);
-        store2<bf16_t>(sWN + j * LD_TK + c, -kex * G0x, -key * G0y);
-        if (NB == 2 && hb < 2) store2<bf16_t>(sKRF + j * LD_TK + c, krx * F0x, kry * F0y);
-        kdx[t] = krx * D0x;
-        kdy[t] = kry * D0y;
+        krx[t] = kx * Rx;
+        kry[t] = ky * Ry;
+        store2<bf16_t>(sKE + j * LD_TK + c, kx * Lx, ky * Ly);
+        store2<bf16_t>(sQE + j * LD_TK + c, qx * Lx, qy * Ly);
+        store2<bf16_t>(sKR + j * LD_TK + c, krx[t], kry[t]);
       }
-      auto st8 = [](bf16_t* dst, const float* x) {
-        *reinterpret_cast<uint4*>(dst) = uint4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                                               pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+      auto st8 = [](bf16_t* dst, const float* x) {     // two 8-byte stores (rows are 8-byte aligned)
+        *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+        *reinterpret_cast<uint2*>(dst + 4) = uint2{pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
       };
-      st8(sKDT + c * LD_CT + 8 * hb, kdx);
-      st8(sKDT + (c + 1) * LD_CT + 8 * hb, kdy);
-      if (hb == 0) *reinterpret_cast<float2*>(sGC + c) = float2{fast_exp2(Hx[0] + Hx[1] + Hx[2] + Hx[3]),
-                                                                fast_exp2(Hy[0] + Hy[1] + Hy[2] + Hy[3])};
+      st8(sKRT + c * LD_CT + 8 * hb, krx);
+      st8(sKRT + (c + 1) * LD_CT + 8 * hb, kry);
+      if (hb == 0) {
+        *reinterpret_cast<float2*>(sG0 + c) = float2{fast_exp2(Hx[0] + Hx[1]), fast_exp2(Hy[0] + Hy[1])};
+        *reinterpret_cast<float2*>(sD0 + c) = float2{fast_exp2(Hx[2] + Hx[3]), fast_exp2(Hy[2] + Hy[3])};
+      }
     }
     if (kwave && tid < CD) sBeta[tid] = tid < nval ? bf2f(rbeta) : 0.0f;
-    const bool bad = kact && fminf(ax, ay) < -thresh;
-    const unsigned long long bal = __ballot(bad);
+    const float worst = fminf(fminf(Hx[0] + Hx[1], Hx[2] + Hx[3]), fminf(Hy[0] + Hy[1], Hy[2] + Hy[3]));
+    const unsigned long long bal = __ballot(kact && worst < -thresh);
     if (lane == 0) sFlag[set * 8 + wave] = bal != 0ull;
   };
 
@@ -341,8 +328,11 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   // Ends before the workgroup barrier that closes the step.
   auto phase2 = [&](int set) __attribute__((always_inline)) {
     const float* sBeta = reinterpret_cast<const float*>(set_base(set) + Cfg::SET_BETA);
-    // A (strictly lower, beta-scaled, fp32) and P (lower, bf16), one 16x16 tile per
-    // wave, computed transposed: lane (g, l16) holds row i = 16I + l16, columns
+    const bf16_t* sKE = reinterpret_cast<const bf16_t*>(set_base(set) + Cfg::SET_KE);
+    const bf16_t* sQE = reinterpret_cast<const bf16_t*>(set_base(set) + Cfg::SET_QE);
+    // A (strictly lower, beta-scaled: diagonal blocks in fp32 for the inverses, -A_10
+    // in bf16 for the V-side) and P (lower, bf16), one 16x16 tile per wave, computed
+    // transposed: lane (g, l16) holds row i = 16I + l16, columns
     // 16J + 4g.., so each lane stores 4 consecutive columns of one row.
     if (wave < 7) {
       const bool isA = wave < 4;
@@ -351,13 +341,13 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       const bool live = I < NB && J <= I;
       floatx4 acc = zero4();
       if (live) {
-        const bf16_t* rows = (J < I) ? sKRF : sKR + 16 * J * LD_TK;   // column tokens j (F-scaled across blocks)
+        const bf16_t* rows = sKR + 16 * J * LD_TK;   // column tokens j
         const bf16_t* cols = isA ? sKE : sQE;
         short8 fa[NS], fb[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          fa[s] = lds_frag(rows, LD_TK, 0, 32 * s, lane);
-          fb[s] = lds_frag(cols, LD_TK, 16 * I, 32 * s, lane);
+          fa[s] = lds_a_perm(rows, LD_TK, 0, 32 * s, lane);      // same depth order on both sides
+          fb[s] = lds_a_perm(cols, LD_TK, 16 * I, 32 * s, lane);
         }
         sched_fence();
 #pragma unroll
@@ -367,69 +357,45 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       float vals[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) vals[r] = live && (isA ? j0 + r < i : j0 + r <= i) ? acc[r] : 0.0f;
-      if (isA) {
+      if (isA && J == I) {                   // diagonal block: fp32 for the inverse
         const float bi = sBeta[i];
         *reinterpret_cast<floatx4*>(sA + i * LD_A + j0) = floatx4{bi * vals[0], bi * vals[1], bi * vals[2], bi * vals[3]};
+      } else if (isA) {                      // A_10: bf16, negated, for the V-side
+        if (live) {
+          const float nb = -sBeta[i];
+          store4_bf16(sA10 + l16 * LD_CT + j0, nb * vals[0], nb * vals[1], nb * vals[2], nb * vals[3]);
+        }
       } else if (live) {
         store4_bf16(sP + i * LD_CT + j0, vals[0], vals[1], vals[2], vals[3]);
       }
     }
     lds_barrier();
-    if (wave == 0) {
-      // diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution: lane (I, j)
-      // holds column j of block I in registers; row i needs rows < i only.  The
-      // strictly-lower rows are loaded up front so that the substitution waits on
-      // LDS a few times rather than once per row.
-      if (lane < 16 * NB) {
-        const int I = lane >> 4, j = lane & 15;
-        float* Ab = sA + 16 * I * LD_A + 16 * I;
-        floatx4 ra[36];                                     // rows 1..15, columns < row, in float4 groups
+    if (wave < NB && lane < 16) {
+      // T_II = (I + A_II)^-1 for I = wave, by column-sweep elimination: lane j holds
+      // column j of T_II; once entry m is final it is eliminated from the rows below,
+      // so each step waits on one FMA only.  The strictly-lower rows of A_II are loaded
+      // up front so that the sweep waits on LDS a few times rather than once per row.
+      const int I = wave, j = lane;
+      const float* Ab = sA + 16 * I * LD_A + 16 * I;
+      floatx4 ra[36];                                       // rows 1..15, columns < row, in float4 groups
 #pragma unroll
-        for (int i = 1, n = 0; i < 16; ++i)
+      for (int i = 1, n = 0; i < 16; ++i)
 #pragma unroll
-          for (int qd = 0; qd < (i + 3) / 4; ++qd, ++n) ra[n] = *reinterpret_cast<const floatx4*>(Ab + i * LD_A + 4 * qd);
-        float t[16];
-        t[0] = j == 0 ? 1.0f : 0.0f;
+        for (int qd = 0; qd < (i + 3) / 4; ++qd, ++n) ra[n] = *reinterpret_cast<const floatx4*>(Ab + i * LD_A + 4 * qd);
+      auto a_at = [&](int i, int m) __attribute__((always_inline)) {   // A_II[i][m], m < i
+        int n = 0;
+        for (int r = 1; r < i; ++r) n += (r + 3) / 4;
+        return ra[n + m / 4][m % 4];
+      };
+      float t[16];
 #pragma unroll
-        for (int i = 1, n = 0; i < 16; ++i) {
-          float a0 = 0.0f, a1 = 0.0f;
+      for (int i = 0; i < 16; ++i) t[i] = i == j ? 1.0f : 0.0f;
 #pragma unroll
-          for (int m = 0; m < i; ++m) {
-            const float a = ra[n + m / 4][m % 4];
-            if (m & 1) a1 += a * t[m];
-            else a0 += a * t[m];
-          }
-          n += (i + 3) / 4;
-          t[i] = (i == j) ? 1.0f : (i > j ? -(a0 + a1) : 0.0f);
-        }
+      for (int m = 0; m < 15; ++m)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          Ab[i * LD_A + j] = t[i];                          // fp32 T_II for the off-diagonal block
-          sT[(16 * I + i) * LD_CT + 16 * I + j] = f2bf(t[i]);
-        }
-      }
-      if (NB == 2) {                           // T_10 = -T_11 (A_10 T_00), fp32 MFMA
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-        floatx4 x = zero4();
+        for (int i = m + 1; i < 16; ++i) t[i] = fmaf(-a_at(i, m), t[m], t[i]);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          x = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 + l16) * LD_A + 4 * s + g], sA[(4 * s + g) * LD_A + l16], x,
-                                                   0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sX[(4 * g + r) * 16 + l16] = x[r];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-        floatx4 y = zero4();
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          y = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 + l16) * LD_A + 16 + 4 * s + g], sX[(4 * s + g) * 16 + l16],
-                                                   y, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sT[(16 + 4 * g + r) * LD_CT + l16] = f2bf(-y[r]);
-      }
+      for (int i = 0; i < 16; ++i) sT[(16 * I + i) * LD_CT + 16 * I + j] = f2bf(t[i]);
     }
   };
 
@@ -440,10 +406,11 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   auto vside = [&](int set, int t0c) __attribute__((always_inline)) {
     const int nval = min(C, T - t0c);
     char* sb = set_base(set);
-    const bf16_t* sWN = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_WN);
-    const bf16_t* sQG = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_QG);
-    const bf16_t* sKDT = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KDT);
-    const float* sGC = reinterpret_cast<const float*>(sb + Cfg::SET_GC);
+    const bf16_t* sKE = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KE);
+    const bf16_t* sQE = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_QE);
+    const bf16_t* sKRT = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KRT);
+    const float* sG0 = reinterpret_cast<const float*>(sb + Cfg::SET_G0);
+    const float* sD0 = reinterpret_cast<const float*>(sb + Cfg::SET_D0);
     const float* sBeta = reinterpret_cast<const float*>(sb + Cfg::SET_BETA);
     // staged values of this wave's 16 columns: slot 2*row + (column / 8)
     const bf16_t* sV = reinterpret_cast<const bf16_t*>(smem + Cfg::OFF_VRAW + set * Cfg::VRAW_BUF + vw * 1024) +
@@ -451,45 +418,56 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     const int col = 16 * vw + l16;
     const bool slow = sFlag[set * 8 + 0] | sFlag[set * 8 + 1] | sFlag[set * 8 + 2] | sFlag[set * 8 + 3];
     if (!slow) {
-      // operands of Y = V - W~ S, loaded as one batch
+      // operands of Yn = KE S~ - V (= -Y), loaded as one batch
       short8 fw[NB][NS];
       bf16_t vv[NB][4];
-      floatx4 bt[NB];
+      floatx4 bt[NB], g0[NMT];
 #pragma unroll
       for (int I = 0; I < NB; ++I) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) fw[I][s] = lds_a_perm(sWN, LD_TK, 16 * I, 32 * s, lane);
+        for (int s = 0; s < NS; ++s) fw[I][s] = lds_a_perm(sKE, LD_TK, 16 * I, 32 * s, lane);
 #pragma unroll
         for (int r = 0; r < 4; ++r) vv[I][r] = sV[(16 * I + 4 * g + r) * 16];
         bt[I] = *reinterpret_cast<const floatx4*>(sBeta + 16 * I + 4 * g);
       }
-      short8 sp[NS];                           // the state as MFMA operand, per 32-row depth slice
 #pragma unroll
-      for (int s = 0; s < NS; ++s) sp[s] = acc_perm(sacc[2 * s], sacc[2 * s + 1]);
+      for (int mt = 0; mt < NMT; ++mt) g0[mt] = *reinterpret_cast<const floatx4*>(sG0 + 16 * mt + 4 * g);
       sched_fence();
-      floatx4 Y[2];
+      // S~ = diag(G0) S in fp32 (kept for the carry) and as MFMA operand per 32-row slice
+      floatx4 st[NMT];
 #pragma unroll
-      for (int I = 0; I < NB; ++I) Y[I] = floatx4{bf2f(vv[I][0]), bf2f(vv[I][1]), bf2f(vv[I][2]), bf2f(vv[I][3])};
+      for (int mt = 0; mt < NMT; ++mt) st[mt] = sacc[mt] * g0[mt];
+      short8 sp[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) sp[s] = acc_perm(st[2 * s], st[2 * s + 1]);
+      floatx4 Yn[2];
+#pragma unroll
+      for (int I = 0; I < NB; ++I)
+        Yn[I] = floatx4{-bf2f(vv[I][0]), -bf2f(vv[I][1]), -bf2f(vv[I][2]), -bf2f(vv[I][3])};
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int I = 0; I < NB; ++I) Y[I] = mfma_bf16(fw[I][s], sp[s], Y[I]);
-      if (NB == 1) Y[1] = zero4();
-      // operands of U = T diag(beta) Y and of o^T = S^T QG^T + U^T P^T
-      short8 ft[NB], fp[NB], fq[NB][NS];
+        for (int I = 0; I < NB; ++I) Yn[I] = mfma_bf16(fw[I][s], sp[s], Yn[I]);
+      // operands of U = (I + A)^-1 diag(beta) Y and of o^T = S~^T QE^T + U^T P^T
+      short8 ft[NB], fp[NB], fq[NB][NS], fa10;
 #pragma unroll
       for (int I = 0; I < NB; ++I) {
         ft[I] = lds_a_perm(sT, LD_CT, 16 * I, 0, lane);
         fp[I] = lds_a_perm(sP, LD_CT, 16 * I, 0, lane);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) fq[I][s] = lds_a_perm(sQG, LD_TK, 16 * I, 32 * s, lane);
+        for (int s = 0; s < NS; ++s) fq[I][s] = lds_a_perm(sQE, LD_TK, 16 * I, 32 * s, lane);
       }
+      if (NB == 2) fa10 = lds_a_perm(sA10, LD_CT, 0, 0, lane);
       sched_fence();
-      const short8 yb = acc_perm(Y[0] * bt[0], NB == 2 ? Y[1] * bt[NB - 1] : zero4());
+      // U_0 = T_00 Z_0, U_1 = T_11 (Z_1 - A_10 U_0), Z = diag(beta) Y = -diag(beta) Yn
       floatx4 U[2];
-#pragma unroll
-      for (int I = 0; I < NB; ++I) U[I] = mfma_bf16(ft[I], yb, zero4());
-      if (NB == 1) U[1] = zero4();
+      U[0] = mfma_bf16(ft[0], acc_perm(Yn[0] * -bt[0], zero4()), zero4());
+      if (NB == 2) {
+        const floatx4 Z1 = mfma_bf16(fa10, acc_perm(U[0], zero4()), Yn[1] * -bt[NB - 1]);
+        U[1] = mfma_bf16(ft[NB - 1], acc_perm(zero4(), Z1), zero4());
+      } else {
+        U[1] = zero4();
+      }
       const short8 ub = acc_perm(U[0], U[1]);
       // o, computed transposed: lane holds token 16I + l16, value columns 16vw + 4g..+3
       floatx4 oT[NB];
@@ -499,17 +477,17 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int I = 0; I < NB; ++I) oT[I] = mfma_bf16(sp[s], fq[I][s], oT[I]);
-      // operands of S = diag(Gamma_C) S + KD^T U
+      // operands of S = diag(D0) (S~ + KR^T U)
       short8 fk[NMT];
-      floatx4 gc[NMT];
+      floatx4 d0[NMT];
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
-        fk[mt] = lds_a_perm(sKDT, LD_CT, 16 * mt, 0, lane);
-        gc[mt] = *reinterpret_cast<const floatx4*>(sGC + 16 * mt + 4 * g);
+        fk[mt] = lds_a_perm(sKRT, LD_CT, 16 * mt, 0, lane);
+        d0[mt] = *reinterpret_cast<const floatx4*>(sD0 + 16 * mt + 4 * g);
       }
       sched_fence();
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) sacc[mt] = mfma_bf16(fk[mt], ub, sacc[mt] * gc[mt]);
+      for (int mt = 0; mt < NMT; ++mt) sacc[mt] = d0[mt] * mfma_bf16(fk[mt], ub, st[mt]);
       if (o) {
         const int c0 = 16 * vw + 4 * g;
 #pragma unroll
@@ -604,6 +582,9 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           if (row < K && col < vcols) sacc[mt][r] = state_in[((size_t)bh * K + row) * V + v0 + col];
         }
     }
+    // Complete the state loads here: inside the walk the wave's only vector-memory
+    // operations are its output stores, which must never hold up the next step.
+    wait_vm();
     lds_barrier();
     for (int c = -1; c < nck; ++c) {
       const int tn = (c + 1) * C;
@@ -633,7 +614,7 @@ hipError_t launch_chunk_fwd_pc_inst(const void* q, const void* k, const void* v,
   const int total = B * H * nvt;
   hipLaunchKernelGGL((chunk_fwd_pc_kernel<KD, VT, C>), dim3(total), dim3(512), 0, s, (const bf16_t*)q,
                      (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)z, A_log, dt_bias, (const bf16_t*)beta,
-                     state_in, scale, (bf16_t*)o, state_out, H, T, K, V, nvt, total, 64.0f);
+                     state_in, scale, (bf16_t*)o, state_out, H, T, K, V, nvt, total, 96.0f);
   return hipGetLastError();
 }
 

@@ -11,7 +11,8 @@
 //   V (waves 4-7):  the state-dependent part, each wave owning 16 value columns and all
 //                   K rows of the fp32 state in accumulator registers: with
 //                   S~ = diag(G0) S,  Y = V - KE S~,  U = (I + A)^-1 diag(beta) Y,
-//                   o = scale (QE S~ + P U),  S = diag(D0) (S~ + KR^T U).
+//                   o = scale (QE S~ + P U),  S = diag(D0) (S~ + KR^T U)  (the state is
+//                   carried as S~ of the next block: one per-channel multiply a block).
 // Step s of the walk runs E on block s+2, W on block s+1 and V on block s side by side
 // and ends with the only workgroup barrier of the step; what a stage writes for block
 // b is read by the next stage one step later, so E's outputs are triple-buffered and
@@ -71,14 +72,16 @@ struct PcCfg {
   static constexpr int SZ_TK = CD * LD_TK * 2;
   static constexpr int SZ_KT = KD * LD_CT * 2;
   static constexpr int SZ_TT = CD * LD_CT * 2;
-  // E outputs of one block (triple-buffered): KE, QE, KR, KR^T, G0, D0, beta
+  // E outputs of one block (triple-buffered): KE, QE, KR, KR^T, G0, D0, beta, and
+  // F = D0 * G0 of the next block (written with the next block)
   static constexpr int SET_KE = 0;
   static constexpr int SET_QE = SET_KE + SZ_TK;
   static constexpr int SET_KR = SET_QE + SZ_TK;
   static constexpr int SET_KRT = SET_KR + SZ_TK;
   static constexpr int SET_G0 = SET_KRT + SZ_KT;
   static constexpr int SET_D0 = SET_G0 + KD * 4;
-  static constexpr int SET_BETA = SET_D0 + KD * 4;
+  static constexpr int SET_F = SET_D0 + KD * 4;
+  static constexpr int SET_BETA = SET_F + KD * 4;
   static constexpr int SET_BYTES = SET_BETA + CD * 4;
   // W outputs of one block (double-buffered): P, T (T_00 and T_11, zero elsewhere),
   // -A_10 (columns 0..15, zero in 16..31)
@@ -330,8 +333,14 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         st8(sKRT + c * LD_CT + 8 * hb, krx);
         st8(sKRT + (c + 1) * LD_CT + 8 * hb, kry);
         if (hb == 0) {
-          *reinterpret_cast<float2*>(sG0 + c) = float2{fast_exp2(Hx[0] + Hx[1]), fast_exp2(Hy[0] + Hy[1])};
+          const float2 g0v = float2{fast_exp2(Hx[0] + Hx[1]), fast_exp2(Hy[0] + Hy[1])};
+          *reinterpret_cast<float2*>(sG0 + c) = g0v;
           *reinterpret_cast<float2*>(sD0 + c) = float2{fast_exp2(Hx[2] + Hx[3]), fast_exp2(Hy[2] + Hy[3])};
+          if (b > 0) {                         // F of the previous block (this lane wrote its D0)
+            char* sp = set_base(b - 1);
+            const float2 dp = *reinterpret_cast<const float2*>(sp + Cfg::SET_D0 + 4 * c);
+            *reinterpret_cast<float2*>(sp + Cfg::SET_F + 4 * c) = float2{dp.x * g0v.x, dp.y * g0v.y};
+          }
         }
       }
       if (tid < CD) sBeta[tid] = tid < nval ? bf2f(rbeta) : 0.0f;
@@ -468,6 +477,11 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     // Complete the state loads here: inside the walk the wave's only vector-memory
     // operations are its output stores, which must never hold up the next step.
     wait_vm();
+    // Between blocks the state is kept as S~ = diag(G0) S of the next block when that
+    // block takes the MFMA path (scaled = true), so a block costs one per-channel
+    // multiply of the state (by F = D0 G0' or, before a token-path block or at the end,
+    // by D0); a block entered unscaled is scaled by its own G0 first.
+    bool scaled = false;
     // output rows of this head through a buffer resource: 32-bit offsets, no 64-bit
     // address arithmetic per store
     const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(o + tb * V, o ? (unsigned)(T * V * 2) : 0u);
@@ -480,7 +494,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       const bf16_t* sQE = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_QE);
       const bf16_t* sKRT = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KRT);
       const float* sG0 = reinterpret_cast<const float*>(sb + Cfg::SET_G0);
-      const float* sD0 = reinterpret_cast<const float*>(sb + Cfg::SET_D0);
+      const bool next_fast = b + 1 < nck && !slow_of(b + 1);
+      const float* sF = reinterpret_cast<const float*>(sb + (next_fast ? Cfg::SET_F : Cfg::SET_D0));
       const float* sBeta = reinterpret_cast<const float*>(sb + Cfg::SET_BETA);
       char* wb = wo_base(b);
       const bf16_t* sP = reinterpret_cast<const bf16_t*>(wb + Cfg::WO_P);
@@ -490,10 +505,14 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       const bf16_t* sV = reinterpret_cast<const bf16_t*>(smem + Cfg::OFF_VRAW + (b % 3) * Cfg::VRAW_BUF + vw * 1024) +
                          (l16 >> 3) * 8 + (l16 & 7);
       if (!slow_of(b)) {
+        if (!scaled) {                         // first block, or after a token-path block
+#pragma unroll
+          for (int mt = 0; mt < NMT; ++mt) sacc[mt] *= *reinterpret_cast<const floatx4*>(sG0 + 16 * mt + 4 * g);
+        }
         // operands of Yn = KE S~ - V (= -Y), loaded as one batch
         short8 fw[NB][NS];
         bf16_t vv[NB][4];
-        floatx4 bt[NB], g0[NMT];
+        floatx4 bt[NB];
 #pragma unroll
         for (int I = 0; I < NB; ++I) {
 #pragma unroll
@@ -502,16 +521,11 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           for (int r = 0; r < 4; ++r) vv[I][r] = sV[(16 * I + 4 * g + r) * 16];
           bt[I] = *reinterpret_cast<const floatx4*>(sBeta + 16 * I + 4 * g);
         }
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) g0[mt] = *reinterpret_cast<const floatx4*>(sG0 + 16 * mt + 4 * g);
         sched_fence();
-        // S~ = diag(G0) S in fp32 (kept for the carry) and as MFMA operand per 32-row slice
-        floatx4 st[NMT];
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) st[mt] = sacc[mt] * g0[mt];
+        // S~ as MFMA operand per 32-row slice
         short8 sp[NS];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) sp[s] = acc_perm(st[2 * s], st[2 * s + 1]);
+        for (int s = 0; s < NS; ++s) sp[s] = acc_perm(sacc[2 * s], sacc[2 * s + 1]);
         floatx4 Yn[2];
 #pragma unroll
         for (int I = 0; I < NB; ++I)
@@ -549,17 +563,18 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         for (int s = 0; s < NS; ++s)
 #pragma unroll
           for (int I = 0; I < NB; ++I) oT[I] = mfma_bf16(sp[s], fq[I][s], oT[I]);
-        // operands of S = diag(D0) (S~ + KR^T U)
+        // operands of S' = diag(F) (S~ + KR^T U), F = D0 G0' (next block scaled) or D0
         short8 fk[NMT];
-        floatx4 d0[NMT];
+        floatx4 fs[NMT];
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
           fk[mt] = lds_a_perm(sKRT, LD_CT, 16 * mt, 0, lane);
-          d0[mt] = *reinterpret_cast<const floatx4*>(sD0 + 16 * mt + 4 * g);
+          fs[mt] = *reinterpret_cast<const floatx4*>(sF + 16 * mt + 4 * g);
         }
         sched_fence();
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) sacc[mt] = d0[mt] * mfma_bf16(fk[mt], ub, st[mt]);
+        for (int mt = 0; mt < NMT; ++mt) sacc[mt] = fs[mt] * mfma_bf16(fk[mt], ub, sacc[mt]);
+        scaled = next_fast;
         if (o) {
           const int c0 = 16 * vw + 4 * g;
 #pragma unroll
@@ -607,6 +622,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           if (g == 0 && col < vcols && o) o[tok * V + v0 + col] = f2bf(op);
         }
         wait_vm();                             // the token path's loads
+        scaled = false;
       }
     };
     for (int s = -2; s < nck; ++s) {

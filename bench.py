@@ -39,12 +39,18 @@ def algorithmic_bytes(wl) -> int:
     return acts + state + params
 
 
+KERNEL_SOURCES = ("kda_chunk_fwd_pc.h", "kda_common.h")
+KERNEL_NAME = "kda::chunk_fwd_pc_kernel<128,64,32>"
+
+
 def kernel_source_hash() -> str:
-    """sha256 of the fused forward kernel's source: counter-measured traffic is only
-    reported while the kernel it was measured on is unchanged."""
+    """sha256 over the sources of the fused bf16 forward kernel: counter-measured traffic
+    is only reported while the kernel it was measured on is unchanged."""
     import hashlib
-    p = os.path.join(ROOT, "gated_delta_rule_47_amd", "csrc", "kda_chunk_fwd.h")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()
+    hs = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        hs.update(open(os.path.join(ROOT, "gated_delta_rule_47_amd", "csrc", name), "rb").read())
+    return hs.hexdigest()
 
 
 def _oracle_head(args):
@@ -158,7 +164,7 @@ def main():
             traffic = None
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "kda::chunk_fwd_kernel", "algorithmic_bytes_per_launch": nbytes,
+            "kernel": KERNEL_NAME, "algorithmic_bytes_per_launch": nbytes,
             "avg_kernel_ms": round(avg_kernel_ms, 4), "min_kernel_ms": round(float(np.min(kern_ms)), 4)}
     cpu = None
     if not args.no_cpu_baseline:

@@ -62,7 +62,8 @@ struct PcCfg {
   static constexpr int VD = round_up(VT, 16);
   static constexpr int NNT = VD / 16;                 // value-column tiles = active V waves
   static constexpr int NMT = KD / 16;                 // key-row tiles of the state
-  static constexpr int NWAVES = 12;
+  static constexpr int NE = 8, NV = 4, NW = 4;        // waves of the E, V and W stages
+  static constexpr int NWAVES = NE + NV + NW;
   // Row strides of the bf16 operand tiles, in elements: 2 (mod 32) banks of 4 bytes per
   // row, so that the 8-byte operand reads (16 consecutive rows per 128-byte LDS cycle)
   // and the 4-byte E writes (rows 8 apart) are free of bank conflicts.
@@ -89,22 +90,17 @@ struct PcCfg {
   static constexpr int WO_T = WO_P + SZ_TT;
   static constexpr int WO_A10 = WO_T + SZ_TT;
   static constexpr int WO_BYTES = WO_A10 + 16 * LD_CT * 2;
-  // staging: per E wave, k, q, z rows of its 32 channels (4 chunks of 16 bytes per row)
-  static constexpr int RAW_T = CD * 64;               // one tensor, 32 rows x 64 bytes
-  static constexpr int RAW_WAVE = 3 * RAW_T;
-  static constexpr int VRAW_BUF = NNT * 1024;         // per value tile: 32 rows x 16 columns
+  static constexpr int VRAW_BUF = NNT * 1024;         // staged v, per value tile: 32 rows x 16 columns
   static constexpr int OFF_SET = 0;
   static constexpr int OFF_WO = OFF_SET + 3 * SET_BYTES;
   static constexpr int OFF_A = OFF_WO + 2 * WO_BYTES;  // diagonal blocks of A (fp32), W scratch
-  static constexpr int OFF_RAW = OFF_A + CD * LD_A * 4;
-  static constexpr int OFF_VRAW = OFF_RAW + 4 * RAW_WAVE;
+  static constexpr int OFF_VRAW = OFF_A + CD * LD_A * 4;
   static constexpr int OFF_FLAG = OFF_VRAW + 3 * VRAW_BUF;
-  static constexpr int TOTAL = OFF_FLAG + 3 * 4 * 4;
-  static constexpr int QKZ_DMA = C / 16;              // 1 KB DMA instructions per tensor, wave and block
+  static constexpr int TOTAL = OFF_FLAG + 3 * NE * 4;
   static_assert(TOTAL <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
-  static_assert(KD % 32 == 0 && (C == 16 || C == 32) && NNT <= 4, "tile shape");
-  static_assert(SET_BYTES % 16 == 0 && WO_BYTES % 16 == 0 && OFF_A % 16 == 0 && OFF_RAW % 16 == 0 &&
-                    OFF_VRAW % 16 == 0 && SET_G0 % 16 == 0,
+  static_assert(KD % 32 == 0 && KD <= 128 && (C == 16 || C == 32) && NNT <= NV, "tile shape");
+  static_assert(SET_BYTES % 16 == 0 && WO_BYTES % 16 == 0 && OFF_A % 16 == 0 && OFF_VRAW % 16 == 0 &&
+                    SET_G0 % 16 == 0,
                 "16-byte alignment");
 };
 
@@ -148,6 +144,9 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, unsig
 // Wait until this wave's outstanding vector-memory operations (its DMAs, loads and
 // stores) have completed.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most 12 of this wave's vector-memory operations are outstanding (they
+// complete in issue order for this count, so every older one has completed).
+__device__ __forceinline__ void wait_vm_but12() { __builtin_amdgcn_s_waitcnt(0x0F7C); }
 // Wait until this wave's outstanding LDS operations have completed.
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
@@ -170,8 +169,81 @@ __device__ __forceinline__ void row_gather(float a, float* H) {
   H[3] = __uint_as_float(p1[1]);
 }
 
+// One block of nval tokens starting at token t0 of a head, token by token, for a wave
+// that owns every key row of 16 value columns (lane = 16g + l16 holds column v0 + col,
+// rows 16*mt + 4g + r) and keeps them in LDS at stl (row tile mt at stl + 256 * mt):
+//   S' = diag(alpha) S,  e = beta (v - S'^T k),  S = S' + k e^T,  o = S^T q_hat.
+// Both reductions over K stay inside the wave.  Used for blocks whose decay is too
+// strong for the factorised MFMA path; kept out of line so that the register budget of
+// the walk is not shaped by this rare path.  Pointers are the head's rows; operands come
+// through buffer resources, four key channels per load.
+template <int NMT>
+__device__ __attribute__((noinline)) void token_block(float* stl, const bf16_t* q, const bf16_t* k,
+                                                     const bf16_t* v, const bf16_t* z, const bf16_t* beta,
+                                                     const float* dt_bias, bf16_t* o, int T, int K, int V, int v0,
+                                                     int vcols, int t0, int nval, float mult2, float scale,
+                                                     int lane, int col) {
+  constexpr unsigned kOOB = 0xFFFFFFF0u;
+  const int g = lane >> 4;
+  const __amdgpu_buffer_rsrc_t tz = make_rsrc(z, (unsigned)(T * K * 2));
+  const __amdgpu_buffer_rsrc_t tk = make_rsrc(k, (unsigned)(T * K * 2));
+  const __amdgpu_buffer_rsrc_t tq = make_rsrc(q, (unsigned)(T * K * 2));
+  const __amdgpu_buffer_rsrc_t tv = make_rsrc(v, (unsigned)(T * V * 2));
+  const __amdgpu_buffer_rsrc_t tbe = make_rsrc(beta, (unsigned)(T * 2));
+  const __amdgpu_buffer_rsrc_t tdb = make_rsrc(dt_bias, dt_bias ? K * 4 : 0u);
+  const __amdgpu_buffer_rsrc_t to = make_rsrc(o, o ? (unsigned)(T * V * 2) : 0u);
+  auto elem = [](u32x2 w, int r) __attribute__((always_inline)) {
+    const uint32_t u = r < 2 ? w.x : w.y;
+    return __uint_as_float((r & 1) ? (u & 0xffff0000u) : (u << 16));
+  };
+  for (int i = 0; i < nval; ++i) {
+    const int tok = t0 + i;
+    const float vv =
+        col < vcols ? bf2f(__builtin_amdgcn_raw_buffer_load_b16(tv, (unsigned)((tok * V + v0 + col) * 2), 0, 0)) : 0.0f;
+    const float bt = bf2f(__builtin_amdgcn_raw_buffer_load_b16(tbe, (unsigned)(tok * 2), 0, 0));
+    float rp = 0.0f;
+    for (int mt = 0; mt < NMT; ++mt) {        // S' = diag(alpha) S, partial S'^T k
+      const int c0 = 16 * mt + 4 * g;
+      const bool ok = c0 < K;                 // K is a multiple of 4
+      const unsigned off = ok ? (unsigned)((tok * K + c0) * 2) : kOOB;
+      const u32x2 zz = __builtin_amdgcn_raw_buffer_load_b64(tz, off, 0, 0);
+      const u32x2 kk = __builtin_amdgcn_raw_buffer_load_b64(tk, off, 0, 0);
+      const floatx4 db =
+          __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(tdb, ok ? (unsigned)(c0 * 4) : kOOB, 0, 0));
+      floatx4 st = *reinterpret_cast<const floatx4*>(stl + mt * 256);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        st[r] *= ok ? fast_exp2(-mult2 * softplus_f(elem(zz, r) + db[r], true)) : 0.0f;
+        rp += st[r] * elem(kk, r);
+      }
+      *reinterpret_cast<floatx4*>(stl + mt * 256) = st;
+    }
+    rp += __shfl_xor(rp, 16);
+    rp += __shfl_xor(rp, 32);
+    const float e = bt * (vv - rp);
+    float op = 0.0f;
+    for (int mt = 0; mt < NMT; ++mt) {        // S += beta k e^T, partial S^T q_hat
+      const int c0 = 16 * mt + 4 * g;
+      const unsigned off = c0 < K ? (unsigned)((tok * K + c0) * 2) : kOOB;
+      const u32x2 kk = __builtin_amdgcn_raw_buffer_load_b64(tk, off, 0, 0);
+      const u32x2 qq = __builtin_amdgcn_raw_buffer_load_b64(tq, off, 0, 0);
+      floatx4 st = *reinterpret_cast<const floatx4*>(stl + mt * 256);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        st[r] += elem(kk, r) * e;
+        op += st[r] * (scale * elem(qq, r));
+      }
+      *reinterpret_cast<floatx4*>(stl + mt * 256) = st;
+    }
+    op += __shfl_xor(op, 16);
+    op += __shfl_xor(op, 32);
+    if (g == 0 && col < vcols)
+      __builtin_amdgcn_raw_buffer_store_b16(f2bf(op), to, (unsigned)((tok * V + v0 + col) * 2), 0, 0);
+  }
+}
+
 template <int KD, int VT, int C>
-__global__ void __launch_bounds__(768)
+__global__ void __launch_bounds__(1024)
 chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                     const bf16_t* __restrict__ z, const float* __restrict__ A_log,
                     const float* __restrict__ dt_bias, const bf16_t* __restrict__ beta,
@@ -186,11 +258,22 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
   float* sA = reinterpret_cast<float*>(smem + Cfg::OFF_A);
   int* sFlag = reinterpret_cast<int*>(smem + Cfg::OFF_FLAG);   // [block % 3][E wave]
-  auto set_base = [&](int b) __attribute__((always_inline)) { return smem + Cfg::OFF_SET + (b % 3) * Cfg::SET_BYTES; };
-  auto wo_base = [&](int b) __attribute__((always_inline)) { return smem + Cfg::OFF_WO + (b & 1) * Cfg::WO_BYTES; };
+  // Buffer offsets of block b, passed through an empty asm so that the compiler keeps them
+  // as one uniform term and folds each tile's constant offset into its LDS instructions.
+  auto set_base = [&](int b) __attribute__((always_inline)) {
+    int off = __builtin_amdgcn_readfirstlane((b % 3) * Cfg::SET_BYTES);
+    asm volatile("" : "+s"(off));
+    return smem + Cfg::OFF_SET + off;
+  };
+  auto wo_base = [&](int b) __attribute__((always_inline)) {
+    int off = __builtin_amdgcn_readfirstlane((b & 1) * Cfg::WO_BYTES);
+    asm volatile("" : "+s"(off));
+    return smem + Cfg::OFF_WO + off;
+  };
   auto slow_of = [&](int b) __attribute__((always_inline)) {
-    const int* f = sFlag + (b % 3) * 4;
-    return (f[0] | f[1] | f[2] | f[3]) != 0;
+    const int4* f = reinterpret_cast<const int4*>(sFlag + (b % 3) * Cfg::NE);
+    const int4 a = f[0], c = f[1];
+    return ((a.x | a.y | a.z | a.w) | (c.x | c.y | c.z | c.w)) != 0;
   };
 
   const int tid = threadIdx.x;
@@ -211,12 +294,20 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   for (int i = tid; i < Cfg::TOTAL / 16; i += NTHR) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
 
   const float mult2 = gate_multiplier(A_log[h]) * kLog2e;
+  constexpr unsigned kOOB = 0xFFFFFFF0u;       // a buffer offset past any range: reads zeros
   lds_barrier();                               // LDS cleared before any DMA lands
 
-  if (wave < 4) {
+  if (wave < Cfg::NE) {
     // ================================================================ E waves
-    const int pair = 16 * wave + l16;          // key-channel pair
-    const int hb = g;                          // 8-token half-block
+    // Wave e covers tokens 16*half .. 16*half+15 of each block (half = e / 4) and key
+    // channels 32*(e % 4) .. +31.  The block's decay reference sits between its two
+    // halves, so a half needs nothing from the other one: the first half's exponents
+    // are minus the decay still to come before the reference, the second half's are
+    // the decay since it.
+    const int half = wave >> 2;
+    const int cw = wave & 3;
+    const int pair = 16 * cw + l16;            // key-channel pair
+    const int qt = g;                          // tokens 16*half + 4*qt .. +3
     const bool kact = 2 * pair < K;
     const bool precise = mult2 > 64.0f * kLog2e;
     const float dtb0 = (kact && dt_bias) ? dt_bias[h * K + 2 * pair] : 0.0f;
@@ -227,23 +318,20 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     const __amdgpu_buffer_rsrc_t rs_z = make_rsrc(z + tb * K, (unsigned)(T * K * 2));
     const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(v + tb * V, (unsigned)(T * V * 2));
     const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(beta + tb, (unsigned)(T * 2));
-    constexpr unsigned kOOB = 0xFFFFFFF0u;     // an offset past any range: zeros
-    char* raw = smem + Cfg::OFF_RAW + wave * Cfg::RAW_WAVE;
 
-    // this wave's channels 32*wave .. +31 of rows [tn, tn + C): instruction j, lane l
-    // fills row 16j + l/4 with channel chunk 4*wave + l%4 (chunks past K read as 0)
-    auto dma_qkz = [&](int tn) __attribute__((always_inline)) {
-      const int ch = 8 * (4 * wave + (lane & 3));
+    // k, q, z of this lane's channel pair and four tokens, one block ahead in registers
+    uint32_t nk[4], nq[4], nz[4];
+    auto load_qkz = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < Cfg::QKZ_DMA; ++j) {
-        const int r = 16 * j + (lane >> 2);
-        const unsigned off = ch < K ? (unsigned)(((tn + r) * K + ch) * 2) : kOOB;
-        dma16(rs_k, raw + j * 1024, off);
-        dma16(rs_q, raw + Cfg::RAW_T + j * 1024, off);
-        dma16(rs_z, raw + 2 * Cfg::RAW_T + j * 1024, off);
+      for (int t = 0; t < 4; ++t) {
+        const int r = 16 * half + 4 * qt + t;
+        const unsigned off = (kact && r < C) ? (unsigned)(((b * C + r) * K + 2 * pair) * 2) : kOOB;
+        nk[t] = buf_load_b32(rs_k, off);
+        nq[t] = buf_load_b32(rs_q, off);
+        nz[t] = buf_load_b32(rs_z, off);
       }
     };
-    // value tile of block b (wave w < NNT: its 16 columns, slot 2*row + half)
+    // value tile of block b into LDS (waves 0 .. NNT-1: 16 columns each, slot 2*row + half)
     auto dma_v = [&](int b) __attribute__((always_inline)) {
       if (wave < NNT) {
         const int r = lane >> 1, c0 = 16 * wave + 8 * (lane & 1);
@@ -251,7 +339,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         dma16(rs_v, smem + Cfg::OFF_VRAW + (b % 3) * Cfg::VRAW_BUF + wave * 1024, off);
       }
     };
-    bf16_t rbeta = 0, rbeta_next = 0;
+    bf16_t rbeta_next = 0;
     auto load_beta = [&](int tn) __attribute__((always_inline)) {
       if (tid < C) rbeta_next = __builtin_amdgcn_raw_buffer_load_b16(rs_b, (unsigned)((tn + tid) * 2), 0, 0);
     };
@@ -268,102 +356,113 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       float* sG0 = reinterpret_cast<float*>(sb + Cfg::SET_G0);
       float* sD0 = reinterpret_cast<float*>(sb + Cfg::SET_D0);
       float* sBeta = reinterpret_cast<float*>(sb + Cfg::SET_BETA);
-      // staged k, q, z of channel pair `pair`, tokens 8hb..8hb+7
-      wait_vm();                               // this wave's DMA of block b (and beta)
-      rbeta = rbeta_next;
-      Pair<bf16_t> rk[8], rq[8], rz[8];
-      {
-        const char* rb = raw + (8 * hb) * 64 + (l16 >> 2) * 16 + (l16 & 3) * 4;
+      Pair<bf16_t> rk[4], rq[4], rz[4];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          rk[t].u = *reinterpret_cast<const uint32_t*>(rb + t * 64);
-          rq[t].u = *reinterpret_cast<const uint32_t*>(rb + Cfg::RAW_T + t * 64);
-          rz[t].u = *reinterpret_cast<const uint32_t*>(rb + 2 * Cfg::RAW_T + t * 64);
-        }
+      for (int t = 0; t < 4; ++t) {
+        rk[t].u = nk[t];
+        rq[t].u = nq[t];
+        rz[t].u = nz[t];
       }
-      wait_lgkm();                             // staging read: it may be refilled now
-      if (b + 1 < nck) {
-        dma_qkz(tn + C);
-        load_beta(tn + C);
-      }
-      if (b < nck) dma_v(b);
+      const bf16_t rbeta = rbeta_next;
+      // Issue this step's memory operations in a fixed order: beta of the next block
+      // (wave 0), the v DMA of this block, then the 12 loads of the next block, so that
+      // waiting for all but the last 12 completes the DMA and keeps the prefetch in flight.
+      if (wave == 0 && b + 1 < nck) load_beta(tn + C);
+      dma_v(b);
+      sched_fence();
+      if (b + 1 < nck) load_qkz(b + 1);
+      sched_fence();
       // Tokens at or past nval (a partial last block, or rows 16..31 when C = 16) are
-      // identity tokens: their staged k and q are 0, and z = -inf makes their gate 0.
-      if (nval < CD) {
-        const int lim = nval - 8 * hb;
+      // identity tokens: their k and q read as 0, and z = -inf makes their gate 0.
+      {
+        const int lim = nval - (16 * half + 4 * qt);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) rz[t].u = t < lim ? rz[t].u : 0xFF80FF80u;
+        for (int t = 0; t < 4; ++t) rz[t].u = t < lim ? rz[t].u : 0xFF80FF80u;
       }
-      // gate in log2 units and its inclusive prefix over the lane's 8 tokens
-      float px[8], py[8];
+      // gate in log2 units and its inclusive prefix over the lane's 4 tokens
+      float px[4], py[4];
       float ax = 0.0f, ay = 0.0f;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < 4; ++t) {
         ax += -mult2 * softplus_f(rz[t].x() + dtb0, PRECISE);
         ay += -mult2 * softplus_f(rz[t].y() + dtb1, PRECISE);
         px[t] = ax;
         py[t] = ay;
       }
-      // the four half-block sums of this channel pair (lanes l16 + 16*hb')
+      // the four quarter sums of this half, channel pair (lanes l16 + 16*j)
       float Hx[4], Hy[4];
       row_gather(ax, Hx);
       row_gather(ay, Hy);
-      // exponent of token t relative to the reference m = H0 + H1: G_t - m
-      const float offx = hb == 0 ? -(Hx[0] + Hx[1]) : hb == 1 ? -Hx[1] : hb == 2 ? 0.0f : Hx[2];
-      const float offy = hb == 0 ? -(Hy[0] + Hy[1]) : hb == 1 ? -Hy[1] : hb == 2 ? 0.0f : Hy[2];
+      const float sumx = (Hx[0] + Hx[1]) + (Hx[2] + Hx[3]);
+      const float sumy = (Hy[0] + Hy[1]) + (Hy[2] + Hy[3]);
+      // exponent of token t relative to the reference: G_t - m = px[t] + off
+      float offx, offy;
+      if (half == 0) {
+        offx = qt == 0 ? -sumx : qt == 1 ? -(Hx[1] + Hx[2] + Hx[3]) : qt == 2 ? -(Hx[2] + Hx[3]) : -Hx[3];
+        offy = qt == 0 ? -sumy : qt == 1 ? -(Hy[1] + Hy[2] + Hy[3]) : qt == 2 ? -(Hy[2] + Hy[3]) : -Hy[3];
+      } else {
+        offx = qt == 0 ? 0.0f : qt == 1 ? Hx[0] : qt == 2 ? Hx[0] + Hx[1] : Hx[0] + Hx[1] + Hx[2];
+        offy = qt == 0 ? 0.0f : qt == 1 ? Hy[0] : qt == 2 ? Hy[0] + Hy[1] : Hy[0] + Hy[1] + Hy[2];
+      }
       if (kact) {
         const int c = 2 * pair;
-        float krx[8], kry[8];
+        float krx[4], kry[4];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < 4; ++t) {
           const float ex = px[t] + offx, ey = py[t] + offy;
           const float Lx = fast_exp2(ex), Ly = fast_exp2(ey), Rx = fast_exp2(-ex), Ry = fast_exp2(-ey);
           const float kx = rk[t].x(), ky = rk[t].y(), qx = rq[t].x(), qy = rq[t].y();
-          const int j = 8 * hb + t;
+          const int j = 16 * half + 4 * qt + t;
           krx[t] = kx * Rx;
           kry[t] = ky * Ry;
           store2<bf16_t>(sKE + j * LD_TK + c, kx * Lx, ky * Ly);
           store2<bf16_t>(sQE + j * LD_TK + c, qx * Lx, qy * Ly);
           store2<bf16_t>(sKR + j * LD_TK + c, krx[t], kry[t]);
         }
-        auto st8 = [](bf16_t* dst, const float* x) {   // two 8-byte stores (rows are 8-byte aligned)
-          *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-          *reinterpret_cast<uint2*>(dst + 4) = uint2{pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
-        };
-        st8(sKRT + c * LD_CT + 8 * hb, krx);
-        st8(sKRT + (c + 1) * LD_CT + 8 * hb, kry);
-        if (hb == 0) {
-          const float2 g0v = float2{fast_exp2(Hx[0] + Hx[1]), fast_exp2(Hy[0] + Hy[1])};
-          *reinterpret_cast<float2*>(sG0 + c) = g0v;
-          *reinterpret_cast<float2*>(sD0 + c) = float2{fast_exp2(Hx[2] + Hx[3]), fast_exp2(Hy[2] + Hy[3])};
-          if (b > 0) {                         // F of the previous block (this lane wrote its D0)
-            char* sp = set_base(b - 1);
-            const float2 dp = *reinterpret_cast<const float2*>(sp + Cfg::SET_D0 + 4 * c);
-            *reinterpret_cast<float2*>(sp + Cfg::SET_F + 4 * c) = float2{dp.x * g0v.x, dp.y * g0v.y};
+        // K R^T rows c, c+1: this lane's four tokens in one 8-byte store each
+        *reinterpret_cast<uint2*>(sKRT + c * LD_CT + 16 * half + 4 * qt) =
+            uint2{pack_bf16x2(krx[0], krx[1]), pack_bf16x2(krx[2], krx[3])};
+        *reinterpret_cast<uint2*>(sKRT + (c + 1) * LD_CT + 16 * half + 4 * qt) =
+            uint2{pack_bf16x2(kry[0], kry[1]), pack_bf16x2(kry[2], kry[3])};
+        if (qt == 0) {
+          const float2 f = float2{fast_exp2(sumx), fast_exp2(sumy)};
+          if (half == 0) {
+            // G0 = 2^m, and F = D0 G0 of the previous block (its D0 was written a step ago)
+            *reinterpret_cast<float2*>(sG0 + c) = f;
+            if (b > 0) {
+              char* sp = set_base(b - 1);
+              const float2 dp = *reinterpret_cast<const float2*>(sp + Cfg::SET_D0 + 4 * c);
+              *reinterpret_cast<float2*>(sp + Cfg::SET_F + 4 * c) = float2{dp.x * f.x, dp.y * f.y};
+            }
+          } else {
+            *reinterpret_cast<float2*>(sD0 + c) = f;   // D0 = 2^(G_last - m)
           }
         }
       }
-      if (tid < CD) sBeta[tid] = tid < nval ? bf2f(rbeta) : 0.0f;
-      const float worst = fminf(fminf(Hx[0] + Hx[1], Hx[2] + Hx[3]), fminf(Hy[0] + Hy[1], Hy[2] + Hy[3]));
-      const unsigned long long bal = __ballot(kact && worst < -thresh);
-      if (lane == 0) sFlag[(b % 3) * 4 + wave] = bal != 0ull;
+      if (wave == 0 && tid < CD) sBeta[tid] = tid < nval ? bf2f(rbeta) : 0.0f;
+      const unsigned long long bal = __ballot(kact && fminf(sumx, sumy) < -thresh);
+      if (lane == 0) sFlag[(b % 3) * Cfg::NE + wave] = bal != 0ull;
     };
 
     if (nck > 0) {
-      dma_qkz(0);
-      load_beta(0);
+      if (wave == 0) load_beta(0);
+      load_qkz(0);
     }
     for (int s = -2; s < nck; ++s) {
-      if (s + 2 < nck) {
-        if (precise) e1(std::true_type{}, s + 2);
-        else e1(std::false_type{}, s + 2);
+      const int b = s + 2;
+      if (b < nck) {
+        if (precise) e1(std::true_type{}, b);
+        else e1(std::false_type{}, b);
       }
-      wait_vm();                               // v rows of block s+2 in LDS before the barrier
+      // v rows of block b (and beta of block b+1) in LDS / registers before the barrier;
+      // the 12 loads of block b+1 may stay in flight
+      if (b + 1 < nck) wait_vm_but12();
+      else wait_vm();
       lds_barrier();
     }
-  } else if (wave >= 8) {
+  } else if (wave >= Cfg::NE + Cfg::NV) {
     // ================================================================ W waves
-    const int ww = wave - 8;
+    const int ww = wave - (Cfg::NE + Cfg::NV);
     auto wstage = [&](int b) __attribute__((always_inline)) {
       char* sb = set_base(b);
       const float* sBeta = reinterpret_cast<const float*>(sb + Cfg::SET_BETA);
@@ -459,7 +558,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     }
   } else {
     // ================================================================ V waves
-    const int vw = wave - 4;
+    const int vw = wave - Cfg::NE;
     const bool vact = vw < NNT;
     const int col = 16 * vw + l16;
     floatx4 sacc[NMT];
@@ -478,22 +577,27 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     // operations are its output stores, which must never hold up the next step.
     wait_vm();
     // Between blocks the state is kept as S~ = diag(G0) S of the next block when that
-    // block takes the MFMA path (scaled = true), so a block costs one per-channel
-    // multiply of the state (by F = D0 G0' or, before a token-path block or at the end,
-    // by D0); a block entered unscaled is scaled by its own G0 first.
-    bool scaled = false;
+    // block takes the MFMA path, and unscaled before a token-path block or at the end:
+    // a block ends with one per-channel multiply of the state, by F = D0 G0' or by D0
+    // (a token-path block by G0' or by nothing), and block 0 is scaled before the walk.
     // output rows of this head through a buffer resource: 32-bit offsets, no 64-bit
     // address arithmetic per store
     const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(o + tb * V, o ? (unsigned)(T * V * 2) : 0u);
 
-    auto vside = [&](int b) __attribute__((always_inline)) {
+    auto vside = [&](auto fast_tag, int b) __attribute__((always_inline)) {
+      constexpr bool FAST = decltype(fast_tag)::value;   // the factorised MFMA path, else token by token
+      // Lane indices through an empty asm: the per-lane offsets derived from them are
+      // recomputed each block instead of occupying registers across the whole walk.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      ln &= 63;                                // a known range lets LDS offsets fold into the loads
+      const int lg = ln >> 4, ll = ln & 15;
       const int t0c = b * C;
       const int nval = min(C, T - t0c);
       char* sb = set_base(b);
       const bf16_t* sKE = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KE);
       const bf16_t* sQE = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_QE);
       const bf16_t* sKRT = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KRT);
-      const float* sG0 = reinterpret_cast<const float*>(sb + Cfg::SET_G0);
       const bool next_fast = b + 1 < nck && !slow_of(b + 1);
       const float* sF = reinterpret_cast<const float*>(sb + (next_fast ? Cfg::SET_F : Cfg::SET_D0));
       const float* sBeta = reinterpret_cast<const float*>(sb + Cfg::SET_BETA);
@@ -503,83 +607,95 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       const bf16_t* sA10 = reinterpret_cast<const bf16_t*>(wb + Cfg::WO_A10);
       // staged values of this wave's 16 columns: slot 2*row + (column / 8)
       const bf16_t* sV = reinterpret_cast<const bf16_t*>(smem + Cfg::OFF_VRAW + (b % 3) * Cfg::VRAW_BUF + vw * 1024) +
-                         (l16 >> 3) * 8 + (l16 & 7);
-      if (!slow_of(b)) {
-        if (!scaled) {                         // first block, or after a token-path block
+                         (ll >> 3) * 8 + (ll & 7);
+      if constexpr (FAST) {
+        // Four phases, each loading its LDS operands as one batch before its MFMAs (the
+        // batches are sized so that the state and the live operands fit the register budget
+        // of a 16-wave workgroup).
+        // (A) Yn = KE S~ - V (= -Y) and o^T = S~^T QE^T (+ U^T P^T below), over the key
+        // depth in rounds of at most two 32-deep slices.  o is computed transposed: ln
+        // holds token 16I + ll, value columns 16vw + 4g..+3.
+        floatx4 Yn[2], oT[NB];
+        {
+          bf16_t vv[NB][4];
 #pragma unroll
-          for (int mt = 0; mt < NMT; ++mt) sacc[mt] *= *reinterpret_cast<const floatx4*>(sG0 + 16 * mt + 4 * g);
-        }
-        // operands of Yn = KE S~ - V (= -Y), loaded as one batch
-        short8 fw[NB][NS];
-        bf16_t vv[NB][4];
-        floatx4 bt[NB];
+          for (int I = 0; I < NB; ++I)
 #pragma unroll
-        for (int I = 0; I < NB; ++I) {
-#pragma unroll
-          for (int s = 0; s < NS; ++s) fw[I][s] = lds_a_perm(sKE, LD_TK, 16 * I, 32 * s, lane);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) vv[I][r] = sV[(16 * I + 4 * g + r) * 16];
-          bt[I] = *reinterpret_cast<const floatx4*>(sBeta + 16 * I + 4 * g);
-        }
-        sched_fence();
-        // S~ as MFMA operand per 32-row slice
-        short8 sp[NS];
-#pragma unroll
-        for (int s = 0; s < NS; ++s) sp[s] = acc_perm(sacc[2 * s], sacc[2 * s + 1]);
-        floatx4 Yn[2];
-#pragma unroll
-        for (int I = 0; I < NB; ++I)
-          Yn[I] = floatx4{-bf2f(vv[I][0]), -bf2f(vv[I][1]), -bf2f(vv[I][2]), -bf2f(vv[I][3])};
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-          for (int I = 0; I < NB; ++I) Yn[I] = mfma_bf16(fw[I][s], sp[s], Yn[I]);
-        // operands of U = (I + A)^-1 diag(beta) Y and of o^T = S~^T QE^T + U^T P^T
-        short8 ft[NB], fp[NB], fq[NB][NS], fa10;
-#pragma unroll
-        for (int I = 0; I < NB; ++I) {
-          ft[I] = lds_a_perm(sT, LD_CT, 16 * I, 0, lane);
-          fp[I] = lds_a_perm(sP, LD_CT, 16 * I, 0, lane);
-#pragma unroll
-          for (int s = 0; s < NS; ++s) fq[I][s] = lds_a_perm(sQE, LD_TK, 16 * I, 32 * s, lane);
-        }
-        if (NB == 2) fa10 = lds_a_perm(sA10, LD_CT, 0, 0, lane);
-        sched_fence();
-        // U_0 = T_00 Z_0, U_1 = T_11 (Z_1 - A_10 U_0), Z = diag(beta) Y = -diag(beta) Yn
-        floatx4 U[2];
-        U[0] = mfma_bf16(ft[0], acc_perm(Yn[0] * -bt[0], zero4()), zero4());
-        if (NB == 2) {
-          const floatx4 Z1 = mfma_bf16(fa10, acc_perm(U[0], zero4()), Yn[1] * -bt[NB - 1]);
-          U[1] = mfma_bf16(ft[NB - 1], acc_perm(zero4(), Z1), zero4());
-        } else {
-          U[1] = zero4();
-        }
-        const short8 ub = acc_perm(U[0], U[1]);
-        // o, computed transposed: lane holds token 16I + l16, value columns 16vw + 4g..+3
-        floatx4 oT[NB];
-#pragma unroll
-        for (int I = 0; I < NB; ++I) oT[I] = mfma_bf16(ub, fp[I], zero4());
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-          for (int I = 0; I < NB; ++I) oT[I] = mfma_bf16(sp[s], fq[I][s], oT[I]);
-        // operands of S' = diag(F) (S~ + KR^T U), F = D0 G0' (next block scaled) or D0
-        short8 fk[NMT];
-        floatx4 fs[NMT];
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
-          fk[mt] = lds_a_perm(sKRT, LD_CT, 16 * mt, 0, lane);
-          fs[mt] = *reinterpret_cast<const floatx4*>(sF + 16 * mt + 4 * g);
-        }
-        sched_fence();
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) sacc[mt] = fs[mt] * mfma_bf16(fk[mt], ub, sacc[mt]);
-        scaled = next_fast;
-        if (o) {
-          const int c0 = 16 * vw + 4 * g;
+            for (int r = 0; r < 4; ++r) vv[I][r] = sV[(16 * I + 4 * lg + r) * 16];
 #pragma unroll
           for (int I = 0; I < NB; ++I) {
-            const int i = 16 * I + l16;
+            Yn[I] = floatx4{-bf2f(vv[I][0]), -bf2f(vv[I][1]), -bf2f(vv[I][2]), -bf2f(vv[I][3])};
+            oT[I] = zero4();
+          }
+        }
+        constexpr int NR = NS > 1 ? 2 : 1;     // slices per round
+#pragma unroll
+        for (int s0 = 0; s0 < NS; s0 += NR) {
+          short8 fw[NB][NR], fq[NB][NR], sp[NR];
+#pragma unroll
+          for (int I = 0; I < NB; ++I)
+#pragma unroll
+            for (int j = 0; j < NR; ++j) {
+              fw[I][j] = lds_a_perm(sKE, LD_TK, 16 * I, 32 * (s0 + j), ln);
+              fq[I][j] = lds_a_perm(sQE, LD_TK, 16 * I, 32 * (s0 + j), ln);
+            }
+          sched_fence();
+#pragma unroll
+          for (int j = 0; j < NR; ++j) sp[j] = acc_perm(sacc[2 * (s0 + j)], sacc[2 * (s0 + j) + 1]);
+#pragma unroll
+          for (int j = 0; j < NR; ++j)
+#pragma unroll
+            for (int I = 0; I < NB; ++I) {
+              Yn[I] = mfma_bf16(fw[I][j], sp[j], Yn[I]);
+              oT[I] = mfma_bf16(sp[j], fq[I][j], oT[I]);
+            }
+        }
+        // (C) U_0 = T_00 Z_0, U_1 = T_11 (Z_1 - A_10 U_0), Z = diag(beta) Y = -diag(beta) Yn
+        short8 ub;
+        {
+          short8 ft[NB], fp[NB], fa10;
+          floatx4 bt[NB];
+#pragma unroll
+          for (int I = 0; I < NB; ++I) {
+            ft[I] = lds_a_perm(sT, LD_CT, 16 * I, 0, ln);
+            fp[I] = lds_a_perm(sP, LD_CT, 16 * I, 0, ln);
+            bt[I] = *reinterpret_cast<const floatx4*>(sBeta + 16 * I + 4 * lg);
+          }
+          if (NB == 2) fa10 = lds_a_perm(sA10, LD_CT, 0, 0, ln);
+          sched_fence();
+          floatx4 U[2];
+          U[0] = mfma_bf16(ft[0], acc_perm(Yn[0] * -bt[0], zero4()), zero4());
+          if (NB == 2) {
+            const floatx4 Z1 = mfma_bf16(fa10, acc_perm(U[0], zero4()), Yn[1] * -bt[NB - 1]);
+            U[1] = mfma_bf16(ft[NB - 1], acc_perm(zero4(), Z1), zero4());
+          } else {
+            U[1] = zero4();
+          }
+          ub = acc_perm(U[0], U[1]);
+#pragma unroll
+          for (int I = 0; I < NB; ++I) oT[I] = mfma_bf16(ub, fp[I], oT[I]);
+        }
+        // (D) S' = diag(F) (S~ + KR^T U), F = D0 G0' (next block scaled) or D0
+        constexpr int DH = NMT > 4 ? 2 : 1;    // in halves of four row tiles when K = 128
+#pragma unroll
+        for (int hd = 0; hd < DH; ++hd) {
+          constexpr int NM = NMT / DH;
+          short8 fk[NM];
+          floatx4 fs[NM];
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            fk[m] = lds_a_perm(sKRT, LD_CT, 16 * (hd * NM + m), 0, ln);
+            fs[m] = *reinterpret_cast<const floatx4*>(sF + 16 * (hd * NM + m) + 4 * lg);
+          }
+          sched_fence();
+#pragma unroll
+          for (int m = 0; m < NM; ++m) sacc[hd * NM + m] = fs[m] * mfma_bf16(fk[m], ub, sacc[hd * NM + m]);
+        }
+        if (o) {
+          const int c0 = 16 * vw + 4 * lg;
+#pragma unroll
+          for (int I = 0; I < NB; ++I) {
+            const int i = 16 * I + ll;
             const u32x2 d = {pack_bf16x2(scale * oT[I][0], scale * oT[I][1]),
                              pack_bf16x2(scale * oT[I][2], scale * oT[I][3])};
             if (i < nval && c0 < vcols)
@@ -587,47 +703,45 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           }
         }
       } else {
-        // token by token: this wave owns every key row of its 16 value columns, so both
-        // reductions over K stay inside the wave
-        for (int i = 0; i < nval; ++i) {
-          const size_t tok = tb + t0c + i;
-          const float vv = col < vcols ? bf2f(v[tok * V + v0 + col]) : 0.0f;
-          const float bt = bf2f(beta[tok]);
-          float rp = 0.0f;
+        // token by token (see token_block): the state waits in LDS meanwhile, in the
+        // operand area of this block's set, which no other stage touches during this step
+        float* stl = reinterpret_cast<float*>(sb) + vw * (NMT * 256) + ln * 4;
 #pragma unroll
-          for (int mt = 0; mt < NMT; ++mt)
+        for (int mt = 0; mt < NMT; ++mt) *reinterpret_cast<floatx4*>(stl + mt * 256) = sacc[mt];
+        token_block<NMT>(stl, q + tb * K, k + tb * K, v + tb * V, z + tb * K, beta + tb,
+                         dt_bias ? dt_bias + h * K : nullptr, o ? o + tb * V : nullptr, T, K, V, v0, vcols, t0c, nval,
+                         mult2, scale, ln, 16 * vw + ll);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {            // S' = diag(alpha) S, partial S'^T k
-              const int c = 16 * mt + 4 * g + r;
-              const bool ok = c < K;
-              const float x = ok ? bf2f(z[tok * K + c]) + (dt_bias ? dt_bias[h * K + c] : 0.0f) : 0.0f;
-              sacc[mt][r] *= ok ? fast_exp2(-mult2 * softplus_f(x, true)) : 0.0f;
-              rp += sacc[mt][r] * (ok ? bf2f(k[tok * K + c]) : 0.0f);
-            }
-          rp += __shfl_xor(rp, 16);
-          rp += __shfl_xor(rp, 32);
-          const float e = bt * (vv - rp);
-          float op = 0.0f;
-#pragma unroll
-          for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {            // S += beta k e^T, partial S^T q_hat
-              const int c = 16 * mt + 4 * g + r;
-              const bool ok = c < K;
-              sacc[mt][r] += (ok ? bf2f(k[tok * K + c]) : 0.0f) * e;
-              op += sacc[mt][r] * (ok ? scale * bf2f(q[tok * K + c]) : 0.0f);
-            }
-          op += __shfl_xor(op, 16);
-          op += __shfl_xor(op, 32);
-          if (g == 0 && col < vcols && o) o[tok * V + v0 + col] = f2bf(op);
-        }
+        for (int mt = 0; mt < NMT; ++mt) sacc[mt] = *reinterpret_cast<const floatx4*>(stl + mt * 256);
         wait_vm();                             // the token path's loads
-        scaled = false;
+        if (next_fast) {
+          const float* sG0n = reinterpret_cast<const float*>(set_base(b + 1) + Cfg::SET_G0);
+#pragma unroll
+          for (int mt = 0; mt < NMT; ++mt) sacc[mt] *= *reinterpret_cast<const floatx4*>(sG0n + 16 * mt + 4 * lg);
+        }
       }
     };
-    for (int s = -2; s < nck; ++s) {
-      if (s >= 0 && vact) vside(s);
-      lds_barrier();
+    lds_barrier();                             // steps -2 and -1: E and W fill the pipeline
+    lds_barrier();
+    if (vact && nck > 0 && !slow_of(0)) {
+      const float* sG00 = reinterpret_cast<const float*>(set_base(0) + Cfg::SET_G0);
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) sacc[mt] *= *reinterpret_cast<const floatx4*>(sG00 + 16 * mt + 4 * g);
+    }
+    // Runs of MFMA-path blocks in an inner loop of their own, so that the rare token-path
+    // block does not shape the register allocation of the common one.  One barrier per step.
+    int s = 0;
+    while (s < nck) {
+      while (s < nck && !slow_of(s)) {
+        if (vact) vside(std::true_type{}, s);
+        lds_barrier();
+        ++s;
+      }
+      if (s < nck) {
+        if (vact) vside(std::false_type{}, s);
+        lds_barrier();
+        ++s;
+      }
     }
     if (vact && state_out) {
 #pragma unroll

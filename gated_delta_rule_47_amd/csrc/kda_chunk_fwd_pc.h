@@ -64,11 +64,14 @@ struct PcCfg {
   static constexpr int NMT = KD / 16;                 // key-row tiles of the state
   static constexpr int NE = 8, NV = 4, NW = 4;        // waves of the E, V and W stages
   static constexpr int NWAVES = NE + NV + NW;
-  // Row strides of the bf16 operand tiles, in elements: 2 (mod 32) banks of 4 bytes per
-  // row, so that the 8-byte operand reads (16 consecutive rows per 128-byte LDS cycle)
-  // and the 4-byte E writes (rows 8 apart) are free of bank conflicts.
-  static constexpr int LD_TK = KD + 4;                // [token][channel] bf16
-  static constexpr int LD_CT = CD + 4;                // [channel|token][token] bf16
+  // Row strides of the bf16 operand tiles, in elements.  Within each 32-wide slice of a
+  // row, the contraction index is stored in the order of perm32(), so that an MFMA operand
+  // fragment is one 16-byte read; the strides put 8 consecutive rows on disjoint banks
+  // (row stride = 4 (mod 32) banks, or 20 for the 40-element rows), which makes those reads
+  // conflict-free, and rows 4 apart 16 banks apart, which does the same for the 4-byte
+  // writes of the E stage.
+  static constexpr int LD_TK = KD + 8;                // [token][channel] bf16
+  static constexpr int LD_CT = CD + 8;                // [channel|token][token] bf16
   static constexpr int LD_A = CD + 4;                 // [token][token] fp32
   static constexpr int SZ_TK = CD * LD_TK * 2;
   static constexpr int SZ_KT = KD * LD_CT * 2;
@@ -104,13 +107,17 @@ struct PcCfg {
                 "16-byte alignment");
 };
 
-// A operand rows [row0, row0+16) with the accumulator-compatible depth order over
-// [d0, d0+32): lane slots 0..3 = depth d0+4g.., slots 4..7 = depth d0+16+4g..
-__device__ __forceinline__ short8 lds_a_perm(const bf16_t* base, int ld, int row0, int d0, int lane) {
-  const bf16_t* p = base + (row0 + (lane & 15)) * ld + d0 + 4 * (lane >> 4);
-  const short4 a = *reinterpret_cast<const short4*>(p);
-  const short4 b = *reinterpret_cast<const short4*>(p + 16);
-  return short8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+// Storage position of contraction index x inside its 32-wide slice: the indices
+// {4g..4g+3, 16+4g..16+4g+3} that lane group g supplies to an MFMA are made contiguous.
+__device__ __forceinline__ constexpr int perm32(int x) {
+  return (x & ~31) + ((x & 15) >> 2) * 8 + ((x & 16) >> 2) + (x & 3);
+}
+
+// MFMA operand rows [row0, row0+16) over the contraction slice [d0, d0+32) (d0 a multiple
+// of 32) from a tile stored in perm32 order: lane (g, l16) gets row row0 + l16, slots 0..3
+// = index d0+4g.., slots 4..7 = index d0+16+4g.. -- the accumulator-compatible order.
+__device__ __forceinline__ short8 lds_frag(const bf16_t* base, int ld, int row0, int d0, int lane) {
+  return *reinterpret_cast<const short8*>(base + (row0 + (lane & 15)) * ld + d0 + 8 * (lane >> 4));
 }
 
 // Operand built from two accumulator tiles (depth rows 0..15 and 16..31).
@@ -307,7 +314,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     const int half = wave >> 2;
     const int cw = wave & 3;
     const int pair = 16 * cw + l16;            // key-channel pair
-    const int qt = g;                          // tokens 16*half + 4*qt .. +3
+    const int pos = g;                          // quarter of the half: tokens 16*half + tq .. +3
+    const int tq = 4 * pos;
     const bool kact = 2 * pair < K;
     const bool precise = mult2 > 64.0f * kLog2e;
     const float dtb0 = (kact && dt_bias) ? dt_bias[h * K + 2 * pair] : 0.0f;
@@ -324,7 +332,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     auto load_qkz = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int r = 16 * half + 4 * qt + t;
+        const int r = 16 * half + tq + t;
         const unsigned off = (kact && r < C) ? (unsigned)(((b * C + r) * K + 2 * pair) * 2) : kOOB;
         nk[t] = buf_load_b32(rs_k, off);
         nq[t] = buf_load_b32(rs_q, off);
@@ -375,7 +383,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       // Tokens at or past nval (a partial last block, or rows 16..31 when C = 16) are
       // identity tokens: their k and q read as 0, and z = -inf makes their gate 0.
       {
-        const int lim = nval - (16 * half + 4 * qt);
+        const int lim = nval - (16 * half + tq);
 #pragma unroll
         for (int t = 0; t < 4; ++t) rz[t].u = t < lim ? rz[t].u : 0xFF80FF80u;
       }
@@ -390,41 +398,42 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         py[t] = ay;
       }
       // the four quarter sums of this half, channel pair (lanes l16 + 16*j)
-      float Hx[4], Hy[4];
-      row_gather(ax, Hx);
-      row_gather(ay, Hy);
-      const float sumx = (Hx[0] + Hx[1]) + (Hx[2] + Hx[3]);
-      const float sumy = (Hy[0] + Hy[1]) + (Hy[2] + Hy[3]);
+      float Qx[4], Qy[4];
+      row_gather(ax, Qx);
+      row_gather(ay, Qy);
+      const float sumx = (Qx[0] + Qx[1]) + (Qx[2] + Qx[3]);
+      const float sumy = (Qy[0] + Qy[1]) + (Qy[2] + Qy[3]);
       // exponent of token t relative to the reference: G_t - m = px[t] + off
       float offx, offy;
       if (half == 0) {
-        offx = qt == 0 ? -sumx : qt == 1 ? -(Hx[1] + Hx[2] + Hx[3]) : qt == 2 ? -(Hx[2] + Hx[3]) : -Hx[3];
-        offy = qt == 0 ? -sumy : qt == 1 ? -(Hy[1] + Hy[2] + Hy[3]) : qt == 2 ? -(Hy[2] + Hy[3]) : -Hy[3];
+        offx = pos == 0 ? -sumx : pos == 1 ? -(Qx[1] + Qx[2] + Qx[3]) : pos == 2 ? -(Qx[2] + Qx[3]) : -Qx[3];
+        offy = pos == 0 ? -sumy : pos == 1 ? -(Qy[1] + Qy[2] + Qy[3]) : pos == 2 ? -(Qy[2] + Qy[3]) : -Qy[3];
       } else {
-        offx = qt == 0 ? 0.0f : qt == 1 ? Hx[0] : qt == 2 ? Hx[0] + Hx[1] : Hx[0] + Hx[1] + Hx[2];
-        offy = qt == 0 ? 0.0f : qt == 1 ? Hy[0] : qt == 2 ? Hy[0] + Hy[1] : Hy[0] + Hy[1] + Hy[2];
+        offx = pos == 0 ? 0.0f : pos == 1 ? Qx[0] : pos == 2 ? Qx[0] + Qx[1] : Qx[0] + Qx[1] + Qx[2];
+        offy = pos == 0 ? 0.0f : pos == 1 ? Qy[0] : pos == 2 ? Qy[0] + Qy[1] : Qy[0] + Qy[1] + Qy[2];
       }
       if (kact) {
         const int c = 2 * pair;
+        const int pc = perm32(c);              // c, c+1 are adjacent in perm32 order
         float krx[4], kry[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const float ex = px[t] + offx, ey = py[t] + offy;
           const float Lx = fast_exp2(ex), Ly = fast_exp2(ey), Rx = fast_exp2(-ex), Ry = fast_exp2(-ey);
           const float kx = rk[t].x(), ky = rk[t].y(), qx = rq[t].x(), qy = rq[t].y();
-          const int j = 16 * half + 4 * qt + t;
+          const int j = 16 * half + tq + t;
           krx[t] = kx * Rx;
           kry[t] = ky * Ry;
-          store2<bf16_t>(sKE + j * LD_TK + c, kx * Lx, ky * Ly);
-          store2<bf16_t>(sQE + j * LD_TK + c, qx * Lx, qy * Ly);
-          store2<bf16_t>(sKR + j * LD_TK + c, krx[t], kry[t]);
+          store2<bf16_t>(sKE + j * LD_TK + pc, kx * Lx, ky * Ly);
+          store2<bf16_t>(sQE + j * LD_TK + pc, qx * Lx, qy * Ly);
+          store2<bf16_t>(sKR + j * LD_TK + pc, krx[t], kry[t]);
         }
         // K R^T rows c, c+1: this lane's four tokens in one 8-byte store each
-        *reinterpret_cast<uint2*>(sKRT + c * LD_CT + 16 * half + 4 * qt) =
+        *reinterpret_cast<uint2*>(sKRT + c * LD_CT + perm32(16 * half + tq)) =
             uint2{pack_bf16x2(krx[0], krx[1]), pack_bf16x2(krx[2], krx[3])};
-        *reinterpret_cast<uint2*>(sKRT + (c + 1) * LD_CT + 16 * half + 4 * qt) =
+        *reinterpret_cast<uint2*>(sKRT + (c + 1) * LD_CT + perm32(16 * half + tq)) =
             uint2{pack_bf16x2(kry[0], kry[1]), pack_bf16x2(kry[2], kry[3])};
-        if (qt == 0) {
+        if (g == 0) {
           const float2 f = float2{fast_exp2(sumx), fast_exp2(sumy)};
           if (half == 0) {
             // G0 = 2^m, and F = D0 G0 of the previous block (its D0 was written a step ago)
@@ -475,28 +484,22 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       bf16_t* sA10 = reinterpret_cast<bf16_t*>(wb + Cfg::WO_A10);
       // tiles of this wave: ww 0: A_00; 1: A_11; 2: A_10 and P_00; 3: P_10 and P_11.
       // Each tile is computed transposed: lane (g, l16) holds row i = 16I + l16,
-      // columns 16J + 4g..+3.
+      // columns 16J + 4g..+3.  The two tiles of a wave share one operand, loaded once.
+      auto frags = [&](const bf16_t* src, int row0, short8* f) __attribute__((always_inline)) {
 #pragma unroll
-      for (int tix = 0; tix < 2; ++tix) {
-        const int kind = ww == 0 ? (tix == 0 ? 0 : -1) : ww == 1 ? (tix == 0 ? 3 : -1)
-                       : ww == 2 ? (tix == 0 ? 1 : 4) : (tix == 0 ? 5 : 6);
-        // kinds: 0 A_00, 1 A_10, 3 A_11, 4 P_00, 5 P_10, 6 P_11
-        if (kind < 0) continue;
-        const bool isA = kind < 4;
-        const int I = (kind == 0 || kind == 4) ? 0 : 1;
-        const int J = (kind == 3 || kind == 6) ? 1 : 0;
-        if (I >= NB) continue;
-        const bf16_t* cols = isA ? sKE : sQE;
-        short8 fa[NS], fb[NS];
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          fa[s] = lds_a_perm(sKR, LD_TK, 16 * J, 32 * s, lane);   // same depth order on both sides
-          fb[s] = lds_a_perm(cols, LD_TK, 16 * I, 32 * s, lane);
-        }
-        sched_fence();
+        for (int s = 0; s < NS; ++s) f[s] = lds_frag(src, LD_TK, row0, 32 * s, lane);  // same depth order on both sides
+      };
+      auto dot = [&](const short8* fa, const short8* fb) __attribute__((always_inline)) {
         floatx4 acc = zero4();
 #pragma unroll
         for (int s = 0; s < NS; ++s) acc = mfma_bf16(fa[s], fb[s], acc);
+        return acc;
+      };
+      // kinds: 0 A_00, 1 A_10, 3 A_11, 4 P_00, 5 P_10, 6 P_11
+      auto put = [&](int kind, floatx4 acc) __attribute__((always_inline)) {
+        const bool isA = kind < 4;
+        const int I = (kind == 0 || kind == 4) ? 0 : 1;
+        const int J = (kind == 3 || kind == 6) ? 1 : 0;
         const int i = 16 * I + l16, j0 = 16 * J + 4 * g;
         float vals[4];
 #pragma unroll
@@ -507,10 +510,33 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
               floatx4{bi * vals[0], bi * vals[1], bi * vals[2], bi * vals[3]};
         } else if (isA) {                      // A_10: bf16, negated, for V
           const float nb = -sBeta[i];
-          store4_bf16(sA10 + l16 * LD_CT + j0, nb * vals[0], nb * vals[1], nb * vals[2], nb * vals[3]);
+          store4_bf16(sA10 + l16 * LD_CT + perm32(j0), nb * vals[0], nb * vals[1], nb * vals[2], nb * vals[3]);
         } else {
-          store4_bf16(sP + i * LD_CT + j0, vals[0], vals[1], vals[2], vals[3]);
+          store4_bf16(sP + i * LD_CT + perm32(j0), vals[0], vals[1], vals[2], vals[3]);
         }
+      };
+      if (ww == 0 || (ww == 1 && NB == 2)) {   // A_II
+        short8 fa[NS], fb[NS];
+        frags(sKR, 16 * ww, fa);
+        frags(sKE, 16 * ww, fb);
+        sched_fence();
+        put(ww == 0 ? 0 : 3, dot(fa, fb));
+      } else if (ww == 2) {                    // A_10 and P_00: KR_0 shared
+        short8 fa[NS], fb[NS], fc[NS];
+        frags(sKR, 0, fa);
+        frags(sQE, 0, fc);
+        if (NB == 2) frags(sKE, 16, fb);
+        sched_fence();
+        put(4, dot(fa, fc));
+        if (NB == 2) put(1, dot(fa, fb));
+      } else if (ww == 3 && NB == 2) {         // P_10 and P_11: QE_1 shared
+        short8 fa[NS], fb[NS], fc[NS];
+        frags(sKR, 0, fa);
+        frags(sKR, 16, fb);
+        frags(sQE, 16, fc);
+        sched_fence();
+        put(5, dot(fa, fc));
+        put(6, dot(fb, fc));
       }
       if (ww < NB) {
         // T_II = (I + A_II)^-1 for I = ww by forward substitution: lane j holds
@@ -547,7 +573,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           rows(std::integral_constant<int, 7>{}, std::integral_constant<int, 12>{});
           rows(std::integral_constant<int, 12>{}, std::integral_constant<int, 16>{});
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sT[(16 * I + i) * LD_CT + 16 * I + j] = f2bf(t[i]);
+          for (int i = 0; i < 16; ++i) sT[(16 * I + i) * LD_CT + perm32(16 * I + j)] = f2bf(t[i]);
         }
       }
     };
@@ -584,7 +610,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     // address arithmetic per store
     const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(o + tb * V, o ? (unsigned)(T * V * 2) : 0u);
 
-    auto vside = [&](auto fast_tag, int b) __attribute__((always_inline)) {
+    auto vside = [&](auto fast_tag, int b, bool next_fast) __attribute__((always_inline)) {
       constexpr bool FAST = decltype(fast_tag)::value;   // the factorised MFMA path, else token by token
       // Lane indices through an empty asm: the per-lane offsets derived from them are
       // recomputed each block instead of occupying registers across the whole walk.
@@ -598,7 +624,6 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       const bf16_t* sKE = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KE);
       const bf16_t* sQE = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_QE);
       const bf16_t* sKRT = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KRT);
-      const bool next_fast = b + 1 < nck && !slow_of(b + 1);
       const float* sF = reinterpret_cast<const float*>(sb + (next_fast ? Cfg::SET_F : Cfg::SET_D0));
       const float* sBeta = reinterpret_cast<const float*>(sb + Cfg::SET_BETA);
       char* wb = wo_base(b);
@@ -636,8 +661,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           for (int I = 0; I < NB; ++I)
 #pragma unroll
             for (int j = 0; j < NR; ++j) {
-              fw[I][j] = lds_a_perm(sKE, LD_TK, 16 * I, 32 * (s0 + j), ln);
-              fq[I][j] = lds_a_perm(sQE, LD_TK, 16 * I, 32 * (s0 + j), ln);
+              fw[I][j] = lds_frag(sKE, LD_TK, 16 * I, 32 * (s0 + j), ln);
+              fq[I][j] = lds_frag(sQE, LD_TK, 16 * I, 32 * (s0 + j), ln);
             }
           sched_fence();
 #pragma unroll
@@ -657,11 +682,11 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           floatx4 bt[NB];
 #pragma unroll
           for (int I = 0; I < NB; ++I) {
-            ft[I] = lds_a_perm(sT, LD_CT, 16 * I, 0, ln);
-            fp[I] = lds_a_perm(sP, LD_CT, 16 * I, 0, ln);
+            ft[I] = lds_frag(sT, LD_CT, 16 * I, 0, ln);
+            fp[I] = lds_frag(sP, LD_CT, 16 * I, 0, ln);
             bt[I] = *reinterpret_cast<const floatx4*>(sBeta + 16 * I + 4 * lg);
           }
-          if (NB == 2) fa10 = lds_a_perm(sA10, LD_CT, 0, 0, ln);
+          if (NB == 2) fa10 = lds_frag(sA10, LD_CT, 0, 0, ln);
           sched_fence();
           floatx4 U[2];
           U[0] = mfma_bf16(ft[0], acc_perm(Yn[0] * -bt[0], zero4()), zero4());
@@ -684,7 +709,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           floatx4 fs[NM];
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
-            fk[m] = lds_a_perm(sKRT, LD_CT, 16 * (hd * NM + m), 0, ln);
+            fk[m] = lds_frag(sKRT, LD_CT, 16 * (hd * NM + m), 0, ln);
             fs[m] = *reinterpret_cast<const floatx4*>(sF + 16 * (hd * NM + m) + 4 * lg);
           }
           sched_fence();
@@ -723,23 +748,30 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     };
     lds_barrier();                             // steps -2 and -1: E and W fill the pipeline
     lds_barrier();
-    if (vact && nck > 0 && !slow_of(0)) {
+    if (vact && nck > 0 && !slow_of(0)) {   // (flags of block 0 were written at step -2)
       const float* sG00 = reinterpret_cast<const float*>(set_base(0) + Cfg::SET_G0);
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) sacc[mt] *= *reinterpret_cast<const floatx4*>(sG00 + 16 * mt + 4 * g);
     }
     // Runs of MFMA-path blocks in an inner loop of their own, so that the rare token-path
     // block does not shape the register allocation of the common one.  One barrier per step.
+    // The flag of block s+1 is read during step s (E wrote it a step earlier), so that no
+    // step starts with an LDS round trip.
     int s = 0;
+    bool slow = nck > 0 && slow_of(0);
     while (s < nck) {
-      while (s < nck && !slow_of(s)) {
-        if (vact) vside(std::true_type{}, s);
+      while (s < nck && !slow) {
+        const bool next_slow = s + 1 < nck && slow_of(s + 1);
+        if (vact) vside(std::true_type{}, s, !next_slow && s + 1 < nck);
         lds_barrier();
+        slow = next_slow;
         ++s;
       }
       if (s < nck) {
-        if (vact) vside(std::false_type{}, s);
+        const bool next_slow = s + 1 < nck && slow_of(s + 1);
+        if (vact) vside(std::false_type{}, s, !next_slow && s + 1 < nck);
         lds_barrier();
+        slow = next_slow;
         ++s;
       }
     }

@@ -277,10 +277,18 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     asm volatile("" : "+s"(off));
     return smem + Cfg::OFF_WO + off;
   };
-  auto slow_of = [&](int b) __attribute__((always_inline)) {
+  auto flags_raw = [&](int b, int4& a, int4& c) __attribute__((always_inline)) {
     const int4* f = reinterpret_cast<const int4*>(sFlag + (b % 3) * Cfg::NE);
-    const int4 a = f[0], c = f[1];
+    a = f[0];
+    c = f[1];
+  };
+  auto any_flag = [](int4 a, int4 c) __attribute__((always_inline)) {
     return ((a.x | a.y | a.z | a.w) | (c.x | c.y | c.z | c.w)) != 0;
+  };
+  auto slow_of = [&](int b) __attribute__((always_inline)) {
+    int4 a, c;
+    flags_raw(b, a, c);
+    return any_flag(a, c);
   };
 
   const int tid = threadIdx.x;
@@ -327,16 +335,21 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(v + tb * V, (unsigned)(T * V * 2));
     const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(beta + tb, (unsigned)(T * 2));
 
-    // k, q, z of this lane's channel pair and four tokens, one block ahead in registers
-    uint32_t nk[4], nq[4], nz[4];
-    auto load_qkz = [&](int b) __attribute__((always_inline)) {
+    // k, q, z of this lane's channel pair and four tokens (and beta, wave 0), loaded one
+    // block ahead into one of two register sets: the walk alternates between them, so a
+    // load never targets registers whose previous contents are still to be read.
+    struct Raw {
+      uint32_t k[4], q[4], z[4];
+      bf16_t beta;
+    };
+    auto load_qkz = [&](int b, Raw& r) __attribute__((always_inline)) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int r = 16 * half + tq + t;
-        const unsigned off = (kact && r < C) ? (unsigned)(((b * C + r) * K + 2 * pair) * 2) : kOOB;
-        nk[t] = buf_load_b32(rs_k, off);
-        nq[t] = buf_load_b32(rs_q, off);
-        nz[t] = buf_load_b32(rs_z, off);
+        const int row = 16 * half + tq + t;
+        const unsigned off = (kact && row < C) ? (unsigned)(((b * C + row) * K + 2 * pair) * 2) : kOOB;
+        r.k[t] = buf_load_b32(rs_k, off);
+        r.q[t] = buf_load_b32(rs_q, off);
+        r.z[t] = buf_load_b32(rs_z, off);
       }
     };
     // value tile of block b into LDS (waves 0 .. NNT-1: 16 columns each, slot 2*row + half)
@@ -347,12 +360,11 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         dma16(rs_v, smem + Cfg::OFF_VRAW + (b % 3) * Cfg::VRAW_BUF + wave * 1024, off);
       }
     };
-    bf16_t rbeta_next = 0;
-    auto load_beta = [&](int tn) __attribute__((always_inline)) {
-      if (tid < C) rbeta_next = __builtin_amdgcn_raw_buffer_load_b16(rs_b, (unsigned)((tn + tid) * 2), 0, 0);
+    auto load_beta = [&](int tn, Raw& r) __attribute__((always_inline)) {
+      r.beta = tid < C ? __builtin_amdgcn_raw_buffer_load_b16(rs_b, (unsigned)((tn + tid) * 2), 0, 0) : (bf16_t)0;
     };
 
-    auto e1 = [&](auto precise_tag, int b) __attribute__((always_inline)) {
+    auto e1 = [&](auto precise_tag, int b, const Raw& cur, Raw& nxt) __attribute__((always_inline)) {
       constexpr bool PRECISE = decltype(precise_tag)::value;
       const int tn = b * C;
       const int nval = min(C, T - tn);
@@ -367,18 +379,19 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       Pair<bf16_t> rk[4], rq[4], rz[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        rk[t].u = nk[t];
-        rq[t].u = nq[t];
-        rz[t].u = nz[t];
+        rk[t].u = cur.k[t];
+        rq[t].u = cur.q[t];
+        rz[t].u = cur.z[t];
       }
-      const bf16_t rbeta = rbeta_next;
+      const bf16_t rbeta = cur.beta;
       // Issue this step's memory operations in a fixed order: beta of the next block
       // (wave 0), the v DMA of this block, then the 12 loads of the next block, so that
       // waiting for all but the last 12 completes the DMA and keeps the prefetch in flight.
-      if (wave == 0 && b + 1 < nck) load_beta(tn + C);
+      // (past the last block these loads fall outside the head's range and read zeros)
+      if (wave == 0) load_beta(tn + C, nxt);
       dma_v(b);
       sched_fence();
-      if (b + 1 < nck) load_qkz(b + 1);
+      load_qkz(b + 1, nxt);
       sched_fence();
       // Tokens at or past nval (a partial last block, or rows 16..31 when C = 16) are
       // identity tokens: their k and q read as 0, and z = -inf makes their gate 0.
@@ -453,21 +466,26 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       if (lane == 0) sFlag[(b % 3) * Cfg::NE + wave] = bal != 0ull;
     };
 
+    Raw ra, rb;
+    ra.beta = rb.beta = 0;
     if (nck > 0) {
-      if (wave == 0) load_beta(0);
-      load_qkz(0);
+      if (wave == 0) load_beta(0, ra);
+      load_qkz(0, ra);
     }
-    for (int s = -2; s < nck; ++s) {
+    auto estep = [&](int s, const Raw& cur, Raw& nxt) __attribute__((always_inline)) {
       const int b = s + 2;
       if (b < nck) {
-        if (precise) e1(std::true_type{}, b);
-        else e1(std::false_type{}, b);
+        if (precise) e1(std::true_type{}, b, cur, nxt);
+        else e1(std::false_type{}, b, cur, nxt);
+        // v rows of block b (and beta of block b+1) in LDS / registers before the barrier;
+        // the 12 loads of block b+1 may stay in flight
+        wait_vm_but12();
       }
-      // v rows of block b (and beta of block b+1) in LDS / registers before the barrier;
-      // the 12 loads of block b+1 may stay in flight
-      if (b + 1 < nck) wait_vm_but12();
-      else wait_vm();
       lds_barrier();
+    };
+    for (int s = -2; s < nck; s += 2) {        // two steps per iteration: block s+2 from ra, s+3 from rb
+      estep(s, ra, rb);
+      if (s + 1 < nck) estep(s + 1, rb, ra);
     }
   } else if (wave >= Cfg::NE + Cfg::NV) {
     // ================================================================ W waves
@@ -610,7 +628,9 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     // address arithmetic per store
     const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(o + tb * V, o ? (unsigned)(T * V * 2) : 0u);
 
-    auto vside = [&](auto fast_tag, int b, bool next_fast) __attribute__((always_inline)) {
+    // nf0, nf1: the raw slow flags of block b+1, loaded at the top of the step and only
+    // examined after phase C, so that their read never stalls the start of a step
+    auto vside = [&](auto fast_tag, int b, int4 nf0, int4 nf1) __attribute__((always_inline)) {
       constexpr bool FAST = decltype(fast_tag)::value;   // the factorised MFMA path, else token by token
       // Lane indices through an empty asm: the per-lane offsets derived from them are
       // recomputed each block instead of occupying registers across the whole walk.
@@ -624,7 +644,6 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       const bf16_t* sKE = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KE);
       const bf16_t* sQE = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_QE);
       const bf16_t* sKRT = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KRT);
-      const float* sF = reinterpret_cast<const float*>(sb + (next_fast ? Cfg::SET_F : Cfg::SET_D0));
       const float* sBeta = reinterpret_cast<const float*>(sb + Cfg::SET_BETA);
       char* wb = wo_base(b);
       const bf16_t* sP = reinterpret_cast<const bf16_t*>(wb + Cfg::WO_P);
@@ -701,6 +720,9 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           for (int I = 0; I < NB; ++I) oT[I] = mfma_bf16(ub, fp[I], oT[I]);
         }
         // (D) S' = diag(F) (S~ + KR^T U), F = D0 G0' (next block scaled) or D0
+        sched_fence();
+        const bool next_fast = b + 1 < nck && !any_flag(nf0, nf1);
+        const float* sF = reinterpret_cast<const float*>(sb + (next_fast ? Cfg::SET_F : Cfg::SET_D0));
         constexpr int DH = NMT > 4 ? 2 : 1;    // in halves of four row tiles when K = 128
 #pragma unroll
         for (int hd = 0; hd < DH; ++hd) {
@@ -739,7 +761,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) sacc[mt] = *reinterpret_cast<const floatx4*>(stl + mt * 256);
         wait_vm();                             // the token path's loads
-        if (next_fast) {
+        if (b + 1 < nck && !any_flag(nf0, nf1)) {
           const float* sG0n = reinterpret_cast<const float*>(set_base(b + 1) + Cfg::SET_G0);
 #pragma unroll
           for (int mt = 0; mt < NMT; ++mt) sacc[mt] *= *reinterpret_cast<const floatx4*>(sG0n + 16 * mt + 4 * lg);
@@ -761,17 +783,19 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     bool slow = nck > 0 && slow_of(0);
     while (s < nck) {
       while (s < nck && !slow) {
-        const bool next_slow = s + 1 < nck && slow_of(s + 1);
-        if (vact) vside(std::true_type{}, s, !next_slow && s + 1 < nck);
+        int4 f0, f1;                           // flags of block s+1 (stale, and unused, past the end)
+        flags_raw(s + 1, f0, f1);
+        if (vact) vside(std::true_type{}, s, f0, f1);
         lds_barrier();
-        slow = next_slow;
+        slow = s + 1 < nck && any_flag(f0, f1);
         ++s;
       }
       if (s < nck) {
-        const bool next_slow = s + 1 < nck && slow_of(s + 1);
-        if (vact) vside(std::false_type{}, s, !next_slow && s + 1 < nck);
+        int4 f0, f1;
+        flags_raw(s + 1, f0, f1);
+        if (vact) vside(std::false_type{}, s, f0, f1);
         lds_barrier();
-        slow = next_slow;
+        slow = s + 1 < nck && any_flag(f0, f1);
         ++s;
       }
     }

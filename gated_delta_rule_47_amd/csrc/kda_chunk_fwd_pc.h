@@ -97,12 +97,16 @@ struct PcCfg {
   static constexpr int OFF_SET = 0;
   static constexpr int OFF_WO = OFF_SET + 3 * SET_BYTES;
   static constexpr int OFF_A = OFF_WO + 2 * WO_BYTES;  // diagonal blocks of A (fp32), W scratch
-  static constexpr int OFF_VRAW = OFF_A + CD * LD_A * 4;
+  // per inverse wave: D^T and D (16 x 20 fp32 each) and M^T (8 x 12 fp32) of the blocked inverse
+  static constexpr int WS_LD = 20, WS_MLD = 12;
+  static constexpr int WS_BYTES = (2 * 16 * WS_LD + 8 * WS_MLD) * 4;
+  static constexpr int OFF_WS = OFF_A + CD * LD_A * 4;
+  static constexpr int OFF_VRAW = OFF_WS + 2 * WS_BYTES;
   static constexpr int OFF_FLAG = OFF_VRAW + 3 * VRAW_BUF;
   static constexpr int TOTAL = OFF_FLAG + 3 * NE * 4;
   static_assert(TOTAL <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
   static_assert(KD % 32 == 0 && KD <= 128 && (C == 16 || C == 32) && NNT <= NV, "tile shape");
-  static_assert(SET_BYTES % 16 == 0 && WO_BYTES % 16 == 0 && OFF_A % 16 == 0 && OFF_VRAW % 16 == 0 &&
+  static_assert(SET_BYTES % 16 == 0 && WO_BYTES % 16 == 0 && OFF_A % 16 == 0 && OFF_WS % 16 == 0 && OFF_VRAW % 16 == 0 &&
                     SET_G0 % 16 == 0,
                 "16-byte alignment");
 };
@@ -557,41 +561,77 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         put(6, dot(fb, fc));
       }
       if (ww < NB) {
-        // T_II = (I + A_II)^-1 for I = ww by forward substitution: lane j holds
-        // column j; row i needs the strictly-lower part of row i and the entries of
-        // rows < i.  Rows are loaded in three batches so that the substitution waits
-        // on LDS a few times rather than once per row.
+        // T_II = (I + N)^-1 for I = ww, N = A_II, in 8 x 8 blocks: with D = diag(T_a, T_b) the
+        // inverses of the diagonal blocks, T = [[T_a, 0], [-T_b N_ba T_a, T_b]].
+        //   1. lanes 0..15: lane j = 8h + jj forward-substitutes column jj of T_a (h = 0) or
+        //      T_b (h = 1) -- seven rows, 28 FMAs -- and writes it to D^T (row j) and D;
+        //   2. all lanes (k, j): M[k][j] = sum_l N_ba[k][l] T_a[l][j]  (8 FMAs);
+        //   3. all lanes (i, j): T_ba[i][j] = -sum_k T_b[i][k] M[k][j]  (8 FMAs).
+        // Each step reads what the previous one wrote in LDS (same wave: in order).
+        const int I = ww;
+        constexpr int WL = Cfg::WS_LD, ML = Cfg::WS_MLD;
+        float* wsDT = reinterpret_cast<float*>(smem + Cfg::OFF_WS + I * Cfg::WS_BYTES);
+        float* wsD = wsDT + 16 * WL;
+        float* wsMT = wsD + 16 * WL;
+        const float* Ab = sA + 16 * I * LD_A + 16 * I;
         wave_lds_fence();                      // this wave's A_II tile
         if (lane < 16) {
-          const int I = ww, j = lane;
-          const float* Ab = sA + 16 * I * LD_A + 16 * I;
-          float t[16];
-          t[0] = j == 0 ? 1.0f : 0.0f;
-          auto rows = [&](auto lo_tag, auto hi_tag) __attribute__((always_inline)) {
-            constexpr int LO = decltype(lo_tag)::value, HI = decltype(hi_tag)::value;
-            floatx4 ra[HI - LO][4];
+          const int h = lane >> 3, jj = lane & 7;
+          const float* Nb = Ab + 8 * h * LD_A + 8 * h;   // diagonal 8 x 8 block h of N
+          floatx4 rlo[8], rhi[8];
 #pragma unroll
-            for (int i = LO; i < HI; ++i)
+          for (int i = 1; i < 8; ++i) {
+            rlo[i] = *reinterpret_cast<const floatx4*>(Nb + i * LD_A);
+            rhi[i] = *reinterpret_cast<const floatx4*>(Nb + i * LD_A + 4);
+          }
+          float t[8];
+          t[0] = jj == 0 ? 1.0f : 0.0f;
 #pragma unroll
-              for (int qd = 0; qd < (i + 3) / 4; ++qd)
-                ra[i - LO][qd] = *reinterpret_cast<const floatx4*>(Ab + i * LD_A + 4 * qd);
+          for (int i = 1; i < 8; ++i) {
+            float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-            for (int i = LO; i < HI; ++i) {
-              float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-              for (int m = 0; m < i - 1; ++m) {
-                if (m & 1) a1 = fmaf(ra[i - LO][m / 4][m % 4], t[m], a1);
-                else a0 = fmaf(ra[i - LO][m / 4][m % 4], t[m], a0);
-              }
-              const float sum = fmaf(ra[i - LO][(i - 1) / 4][(i - 1) % 4], t[i - 1], a0 + a1);
-              t[i] = i == j ? 1.0f : -sum;
+            for (int m = 0; m < i; ++m) {
+              const float nim = m < 4 ? rlo[i][m] : rhi[i][m - 4];
+              if (m & 1) a1 = fmaf(nim, t[m], a1);
+              else a0 = fmaf(nim, t[m], a0);
             }
-          };
-          rows(std::integral_constant<int, 1>{}, std::integral_constant<int, 7>{});
-          rows(std::integral_constant<int, 7>{}, std::integral_constant<int, 12>{});
-          rows(std::integral_constant<int, 12>{}, std::integral_constant<int, 16>{});
+            t[i] = i == jj ? 1.0f : -(a0 + a1);
+          }
+          float* dt = wsDT + lane * WL + 8 * h;          // D^T row j: column j of D
+          *reinterpret_cast<floatx4*>(dt) = floatx4{t[0], t[1], t[2], t[3]};
+          *reinterpret_cast<floatx4*>(dt + 4) = floatx4{t[4], t[5], t[6], t[7]};
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sT[(16 * I + i) * LD_CT + perm32(16 * I + j)] = f2bf(t[i]);
+          for (int i = 0; i < 8; ++i) {
+            wsD[(8 * h + i) * WL + lane] = t[i];
+            sT[(16 * I + 8 * h + i) * LD_CT + perm32(16 * I + lane)] = f2bf(t[i]);
+          }
+        }
+        const int ki = lane >> 3, j = lane & 7;
+        {
+          const floatx4 n0 = *reinterpret_cast<const floatx4*>(Ab + (8 + ki) * LD_A);
+          const floatx4 n1 = *reinterpret_cast<const floatx4*>(Ab + (8 + ki) * LD_A + 4);
+          const floatx4 t0 = *reinterpret_cast<const floatx4*>(wsDT + j * WL);
+          const floatx4 t1 = *reinterpret_cast<const floatx4*>(wsDT + j * WL + 4);
+          float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+          for (int l = 0; l < 4; ++l) {
+            m0 = fmaf(n0[l], t0[l], m0);
+            m1 = fmaf(n1[l], t1[l], m1);
+          }
+          wsMT[j * ML + ki] = m0 + m1;         // M^T[j][k]
+        }
+        {
+          const floatx4 b0 = *reinterpret_cast<const floatx4*>(wsD + (8 + ki) * WL + 8);
+          const floatx4 b1 = *reinterpret_cast<const floatx4*>(wsD + (8 + ki) * WL + 12);
+          const floatx4 c0 = *reinterpret_cast<const floatx4*>(wsMT + j * ML);
+          const floatx4 c1 = *reinterpret_cast<const floatx4*>(wsMT + j * ML + 4);
+          float u0 = 0.0f, u1 = 0.0f;
+#pragma unroll
+          for (int k4 = 0; k4 < 4; ++k4) {
+            u0 = fmaf(b0[k4], c0[k4], u0);
+            u1 = fmaf(b1[k4], c1[k4], u1);
+          }
+          sT[(16 * I + 8 + ki) * LD_CT + perm32(16 * I + j)] = f2bf(-(u0 + u1));
         }
       }
     };

@@ -493,6 +493,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     }
   } else if (wave >= Cfg::NE + Cfg::NV) {
     // ================================================================ W waves
+    __builtin_amdgcn_s_setprio(2);             // issue ahead of the E waves (see the V waves)
     const int ww = wave - (Cfg::NE + Cfg::NV);
     auto wstage = [&](int b) __attribute__((always_inline)) {
       char* sb = set_base(b);
@@ -642,6 +643,9 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     }
   } else {
     // ================================================================ V waves
+    // The state chain is the walk's critical path and shares each SIMD with two E waves
+    // that have slack: the highest issue priority lets it go first whenever it is ready.
+    __builtin_amdgcn_s_setprio(3);
     const int vw = wave - Cfg::NE;
     const bool vact = vw < NNT;
     const int col = 16 * vw + l16;

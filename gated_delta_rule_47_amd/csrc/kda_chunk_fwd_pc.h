@@ -1,33 +1,35 @@
 // Pipelined chunked KDA forward for bf16 activations on gfx950.
 //
-// One workgroup of 12 waves owns one (batch, head, value tile of <= 64 columns) and
+// One workgroup of 16 waves owns one (batch, head, value tile of <= 64 columns) and
 // walks the sequence in blocks of C <= 32 tokens.  The work of a block b splits into
-// three stages, each done by its own four waves:
-//   E (waves 0-3):  the gate and block-local decay scans and the decay-weighted
-//                   operands KE, QE, KR (and KR^T), from q, k, z staged in LDS;
-//   W (waves 8-11): the strictly-lower A = diag(beta) KE KR^T and the lower
-//                   P = QE KR^T (MFMA), and the inverses T_00, T_11 of the two 16x16
-//                   diagonal blocks of I + A (column-sweep elimination);
-//   V (waves 4-7):  the state-dependent part, each wave owning 16 value columns and all
-//                   K rows of the fp32 state in accumulator registers: with
-//                   S~ = diag(G0) S,  Y = V - KE S~,  U = (I + A)^-1 diag(beta) Y,
-//                   o = scale (QE S~ + P U),  S = diag(D0) (S~ + KR^T U)  (the state is
-//                   carried as S~ of the next block: one per-channel multiply a block).
+// three stages, each done by its own waves:
+//   E (waves 0-7):   the gate and block-local decay scans and the decay-weighted
+//                    operands KE, QE, KR (and KR^T); wave e covers one 16-token half of
+//                    the block and 32 key channels, from q, k, z loaded straight into
+//                    registers one block ahead;
+//   V (waves 8-11):  the state-dependent part, each wave owning 16 value columns and all
+//                    K rows of the fp32 state in accumulator registers: with
+//                    S~ = diag(G0) S,  Y = V - KE S~,  U = (I + A)^-1 diag(beta) Y,
+//                    o = scale (QE S~ + P U),  S = diag(D0) (S~ + KR^T U)  (the state is
+//                    carried as S~ of the next block: one per-channel multiply a block);
+//   W (waves 12-15): the strictly-lower A = diag(beta) KE KR^T and the lower
+//                    P = QE KR^T (MFMA), and the inverses T_00, T_11 of the two 16x16
+//                    diagonal blocks of I + A (in 8 x 8 blocks: two short substitutions,
+//                    then the off-diagonal block from two small products).
 // Step s of the walk runs E on block s+2, W on block s+1 and V on block s side by side
 // and ends with the only workgroup barrier of the step; what a stage writes for block
 // b is read by the next stage one step later, so E's outputs are triple-buffered and
-// W's double-buffered in LDS.  Only V depends on the state.
+// W's double-buffered in LDS.  Only V depends on the state; it runs at the highest
+// wave priority, W next, E (which has slack) last.
 //
 // (U = (I + A)^-1 diag(beta) (V - W~ S) is the u - w S of the WY form with the product
 // w = T diag(beta) W~ folded into the state-dependent side.  V applies the inverse
 // blockwise, U_0 = T_00 Z_0 and U_1 = T_11 (Z_1 - A_10 U_0) with Z = diag(beta) Y, so the
-// off-diagonal block of the inverse is never formed.)
+// off-diagonal block of the inverse is never formed.  E stores KE negated and QE with
+// the read scale folded in, so that V needs neither a sign flip nor a scaling of o.)
 //
-// Activations reach LDS by buffer-to-LDS DMA (16 bytes per lane, 1 KB per instruction),
-// issued by the E waves: each E wave stages the q, k, z rows of its own 32 channels one
-// block ahead into a private area (it alone reads them, so its own wait on the DMA is
-// the only synchronisation), and the v rows of block s+2 into a triple-buffered area
-// that V reads after the step barriers in between.
+// The v rows of each block reach LDS by buffer-to-LDS DMA (16 bytes per lane), issued by
+// E waves two steps before V reads them.
 //
 // V chains MFMA results into MFMAs without LDS: a 32-deep contraction over two 16-row
 // accumulator tiles is fed with lane l supplying depth {4g..4g+3} of the first tile and
@@ -441,8 +443,10 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           const int j = 16 * half + tq + t;
           krx[t] = kx * Rx;
           kry[t] = ky * Ry;
-          store2<bf16_t>(sKE + j * LD_TK + pc, kx * Lx, ky * Ly);
-          store2<bf16_t>(sQE + j * LD_TK + pc, qx * Lx, qy * Ly);
+          // KE is stored negated and QE with the read scale folded in (the V stage then
+          // needs neither a sign flip of v nor a scaling of o)
+          store2<bf16_t>(sKE + j * LD_TK + pc, -kx * Lx, -ky * Ly);
+          store2<bf16_t>(sQE + j * LD_TK + pc, scale * (qx * Lx), scale * (qy * Ly));
           store2<bf16_t>(sKR + j * LD_TK + pc, krx[t], kry[t]);
         }
         // K R^T rows c, c+1: this lane's four tokens in one 8-byte store each
@@ -528,11 +532,11 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
 #pragma unroll
         for (int r = 0; r < 4; ++r) vals[r] = (isA ? j0 + r < i : j0 + r <= i) ? acc[r] : 0.0f;
         if (isA && I == J) {                   // diagonal block: fp32 for the inverse
-          const float bi = sBeta[i];
+          const float bi = -sBeta[i];          // (the tile is -A: KE is stored negated)
           *reinterpret_cast<floatx4*>(sA + i * LD_A + j0) =
               floatx4{bi * vals[0], bi * vals[1], bi * vals[2], bi * vals[3]};
         } else if (isA) {                      // A_10: bf16, negated, for V
-          const float nb = -sBeta[i];
+          const float nb = sBeta[i];           // (the tile is -A_10)
           store4_bf16(sA10 + l16 * LD_CT + perm32(j0), nb * vals[0], nb * vals[1], nb * vals[2], nb * vals[3]);
         } else {
           store4_bf16(sP + i * LD_CT + perm32(j0), vals[0], vals[1], vals[2], vals[3]);
@@ -700,10 +704,11 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         // Four phases, each loading its LDS operands as one batch before its MFMAs (the
         // batches are sized so that the state and the live operands fit the register budget
         // of a 16-wave workgroup).
-        // (A) Yn = KE S~ - V (= -Y) and o^T = S~^T QE^T (+ U^T P^T below), over the key
+        // (A) Y = V - KE S~ (accumulated as V + (-KE) S~: KE is stored negated) and
+        // o^T = S~^T QE^T (+ U^T P^T below; QE and P carry the read scale), over the key
         // depth in rounds of at most two 32-deep slices.  o is computed transposed: ln
         // holds token 16I + ll, value columns 16vw + 4g..+3.
-        floatx4 Yn[2], oT[NB];
+        floatx4 Y[2], oT[NB];
         {
           bf16_t vv[NB][4];
 #pragma unroll
@@ -712,7 +717,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
             for (int r = 0; r < 4; ++r) vv[I][r] = sV[(16 * I + 4 * lg + r) * 16];
 #pragma unroll
           for (int I = 0; I < NB; ++I) {
-            Yn[I] = floatx4{-bf2f(vv[I][0]), -bf2f(vv[I][1]), -bf2f(vv[I][2]), -bf2f(vv[I][3])};
+            Y[I] = floatx4{bf2f(vv[I][0]), bf2f(vv[I][1]), bf2f(vv[I][2]), bf2f(vv[I][3])};
             oT[I] = zero4();
           }
         }
@@ -734,11 +739,11 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           for (int j = 0; j < NR; ++j)
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
-              Yn[I] = mfma_bf16(fw[I][j], sp[j], Yn[I]);
+              Y[I] = mfma_bf16(fw[I][j], sp[j], Y[I]);
               oT[I] = mfma_bf16(sp[j], fq[I][j], oT[I]);
             }
         }
-        // (C) U_0 = T_00 Z_0, U_1 = T_11 (Z_1 - A_10 U_0), Z = diag(beta) Y = -diag(beta) Yn
+        // (C) U_0 = T_00 Z_0, U_1 = T_11 (Z_1 - A_10 U_0), Z = diag(beta) Y (fa10 holds -beta A_10)
         short8 ub;
         {
           short8 ft[NB], fp[NB], fa10;
@@ -752,9 +757,9 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           if (NB == 2) fa10 = lds_frag(sA10, LD_CT, 0, 0, ln);
           sched_fence();
           floatx4 U[2];
-          U[0] = mfma_bf16(ft[0], acc_perm(Yn[0] * -bt[0], zero4()), zero4());
+          U[0] = mfma_bf16(ft[0], acc_perm(Y[0] * bt[0], zero4()), zero4());
           if (NB == 2) {
-            const floatx4 Z1 = mfma_bf16(fa10, acc_perm(U[0], zero4()), Yn[1] * -bt[NB - 1]);
+            const floatx4 Z1 = mfma_bf16(fa10, acc_perm(U[0], zero4()), Y[1] * bt[NB - 1]);
             U[1] = mfma_bf16(ft[NB - 1], acc_perm(zero4(), Z1), zero4());
           } else {
             U[1] = zero4();
@@ -787,8 +792,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
 #pragma unroll
           for (int I = 0; I < NB; ++I) {
             const int i = 16 * I + ll;
-            const u32x2 d = {pack_bf16x2(scale * oT[I][0], scale * oT[I][1]),
-                             pack_bf16x2(scale * oT[I][2], scale * oT[I][3])};
+            const u32x2 d = {pack_bf16x2(oT[I][0], oT[I][1]), pack_bf16x2(oT[I][2], oT[I][3])};
             if (i < nval && c0 < vcols)
               __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, (unsigned)(((t0c + i) * V + v0 + c0) * 2), 0, 0);
           }

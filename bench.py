@@ -62,22 +62,60 @@ def _oracle_head(args):
     wl = ks.WORKLOADS[wl_name]
     A_log, dt_bias = ks.head_params(wl)
     sl = ks.head_slice(wl, b, h)
-    t0 = time.perf_counter()
+    t0 = time.time()
     g, _ = R.gate(sl["z"][None, None], A_log[h:h + 1], dt_bias[h:h + 1])
     R.recurrent(sl["q"][None, None], sl["k"][None, None], sl["v"][None, None], g, sl["beta"][None, None],
                 sl["state_in"][None, None])
-    return time.perf_counter() - t0
+    return t0, time.time()
 
 
 def cpu_baseline(wl, n_heads: int, workers: int) -> dict:
+    """The f64 oracle (gate + token recurrence) on n_heads whole heads, one per process:
+    head-tokens per second of wall time from the first head's start to the last head's
+    end (input generation excluded)."""
     heads = [(i // wl.H % wl.B, i % wl.H) for i in range(n_heads)]
-    t0 = time.perf_counter()
     with ProcessPoolExecutor(workers) as ex:
-        list(ex.map(_oracle_head, [(wl.name, b, h) for b, h in heads]))
-    wall = time.perf_counter() - t0
+        spans = list(ex.map(_oracle_head, [(wl.name, b, h) for b, h in heads]))
+    wall = max(e for _, e in spans) - min(s for s, _ in spans)
+    cpu = sum(e - s for s, e in spans)
     return {"value": n_heads * wl.T / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
-            "sample": "%d of %d heads at full T=%d (f64 numpy token recurrence, one head per process, "
-                      "%.1f s wall)" % (n_heads, wl.B * wl.H, wl.T, wall)}
+            "sample": "%d of %d heads at full T=%d (f64 numpy token recurrence, one head per process; "
+                      "%.1f s wall, %.1f s of CPU work)" % (n_heads, wl.B * wl.H, wl.T, wall, cpu)}
+
+
+def _pmc_per_dispatch(directory: str, counter: str, kernel_match: str) -> list:
+    """Per-dispatch sums of one rocprofv3 --pmc counter (CSV output) for matching kernels."""
+    import collections
+    import csv
+    rows = csv.DictReader(open(os.path.join(directory, "run_counter_collection.csv")))
+    agg = collections.defaultdict(float)
+    for r in rows:
+        if r["Counter_Name"] == counter and kernel_match in r["Kernel_Name"]:
+            agg[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return list(agg.values())
+
+
+def traffic_from_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, workload, out_path):
+    """HBM bytes per launch of the fused forward from two counter runs (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch), each calibrated by the same counter on a plain device
+    copy of known size: factor = counter KiB * 1024 / copied bytes."""
+    f = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "chunk_fwd_pc")
+    w = _pmc_per_dispatch(write_dir, "WRITE_SIZE", "chunk_fwd_pc")
+    cf = _pmc_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    cw = _pmc_per_dispatch(copy_write_dir, "WRITE_SIZE", "copyBuffer")
+    if not (f and w and cf and cw):
+        raise SystemExit("missing dispatches in the counter files")
+    nbytes = copy_mib * (1 << 20)
+    mean = lambda x: sum(x) / len(x)
+    ff, wf = mean(cf) * 1024 / nbytes, mean(cw) * 1024 / nbytes
+    fb, wb = mean(f) * 1024 / ff, mean(w) * 1024 / wf
+    out = {"workload": workload, "kernel": KERNEL_NAME, "kernel_source_sha256": kernel_source_hash(),
+           "fetch_size_kib_per_dispatch": mean(f), "write_size_kib_per_dispatch": mean(w),
+           "copy_calibration": {"bytes": nbytes, "fetch_size_kib": mean(cf), "write_size_kib": mean(cw),
+                                "fetch_factor": ff, "write_factor": wf},
+           "fetch_bytes_per_launch": int(fb), "write_bytes_per_launch": int(wb), "bytes_per_launch": int(fb + wb)}
+    json.dump(out, open(out_path, "w"), indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def main():
@@ -92,7 +130,14 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device-to-device copy of this many MiB "
                          "(--steps times), to calibrate the FETCH_SIZE/WRITE_SIZE counters")
+    ap.add_argument("--traffic-from-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write --traffic-json from rocprofv3 --pmc CSV directories of the kernel (FETCH_SIZE, "
+                         "WRITE_SIZE) and of a --copy-calibration-mib run (same counters); no GPU work")
+    ap.add_argument("--calibration-mib", type=int, default=1024, help="size of the calibration copy, MiB")
     args = ap.parse_args()
+    if args.traffic_from_pmc:
+        traffic_from_pmc(*args.traffic_from_pmc, args.calibration_mib, args.workload, args.traffic_json)
+        return
     if args.copy_calibration_mib:
         import torch
         n = args.copy_calibration_mib * (1 << 20)

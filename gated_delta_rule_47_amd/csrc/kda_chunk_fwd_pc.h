@@ -68,11 +68,13 @@ struct PcCfg {
   static constexpr int NWAVES = NE + NV + NW;
   // Row strides of the bf16 operand tiles, in elements.  Within each 32-wide slice of a
   // row, the contraction index is stored in the order of perm32(), so that an MFMA operand
-  // fragment is one 16-byte read; the strides put 8 consecutive rows on disjoint banks
-  // (row stride = 4 (mod 32) banks, or 20 for the 40-element rows), which makes those reads
-  // conflict-free, and rows 4 apart 16 banks apart, which does the same for the 4-byte
-  // writes of the E stage.
-  static constexpr int LD_TK = KD + 8;                // [token][channel] bf16
+  // fragment is one 16-byte read.  Measured on gfx950, 16-byte reads of 16 rows are free of
+  // bank conflicts for row strides of 96 or 288 bytes but run at half rate for 80 or 272
+  // bytes, while the 4-byte writes of the E stage (rows 4 apart) cost the same for all of
+  // them: the [token][channel] tiles, read most, take KD + 16 (288 bytes when K = 128); the
+  // 32-token rows keep CD + 8 (80 bytes: the larger stride would not fit in LDS, and their
+  // 8-byte row stores conflict at 96).
+  static constexpr int LD_TK = KD + 16;               // [token][channel] bf16
   static constexpr int LD_CT = CD + 8;                // [channel|token][token] bf16
   static constexpr int LD_A = CD + 4;                 // [token][token] fp32
   static constexpr int SZ_TK = CD * LD_TK * 2;

@@ -15,21 +15,23 @@
 //   W (waves 12-15): the strictly-lower A = diag(beta) KE KR^T and the lower
 //                    P = QE KR^T (MFMA), and the inverses T_00, T_11 of the two 16x16
 //                    diagonal blocks of I + A (in 8 x 8 blocks: two short substitutions,
-//                    then the off-diagonal block from two small products).
+//                    then the off-diagonal block from two small products); W also
+//                    stages v and beta of the block after next.
 // Step s of the walk runs E on block s+2, W on block s+1 and V on block s side by side
 // and ends with the only workgroup barrier of the step; what a stage writes for block
 // b is read by the next stage one step later, so E's outputs are triple-buffered and
 // W's double-buffered in LDS.  Only V depends on the state; it runs at the highest
-// wave priority, W next, E (which has slack) last.
+// wave priority, W next, E last.
 //
 // (U = (I + A)^-1 diag(beta) (V - W~ S) is the u - w S of the WY form with the product
 // w = T diag(beta) W~ folded into the state-dependent side.  V applies the inverse
 // blockwise, U_0 = T_00 Z_0 and U_1 = T_11 (Z_1 - A_10 U_0) with Z = diag(beta) Y, so the
-// off-diagonal block of the inverse is never formed.  E stores KE negated and QE with
-// the read scale folded in, so that V needs neither a sign flip nor a scaling of o.)
+// off-diagonal block of the inverse is never formed.  E stores KE negated, so that V
+// needs no sign flip of v.)
 //
 // The v rows of each block reach LDS by buffer-to-LDS DMA (16 bytes per lane), issued by
-// E waves two steps before V reads them.
+// W waves two steps before V reads them.  The E waves' only memory operations are their
+// register loads, so waiting for one block's loads never waits for anything younger.
 //
 // V chains MFMA results into MFMAs without LDS: a 32-deep contraction over two 16-row
 // accumulator tiles is fed with lane l supplying depth {4g..4g+3} of the first tile and
@@ -159,9 +161,6 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, unsig
 // Wait until this wave's outstanding vector-memory operations (its DMAs, loads and
 // stores) have completed.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// Wait until at most 12 of this wave's vector-memory operations are outstanding (they
-// complete in issue order for this count, so every older one has completed).
-__device__ __forceinline__ void wait_vm_but12() { __builtin_amdgcn_s_waitcnt(0x0F7C); }
 // Wait until this wave's outstanding LDS operations have completed.
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
@@ -172,16 +171,19 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
-// Values of `a` held by the lanes 16*j + (lane % 16), j = 0..3, delivered to every lane
-// (two permlane swaps, no LDS).
-__device__ __forceinline__ void row_gather(float a, float* H) {
+// For the values a_j of `a` held by the lanes 16j + (lane % 16), j = 0..3: their total
+// (a_0 + a_1) + (a_2 + a_3) in every lane, and in lane 16g + (lane % 16) the sum of the
+// a_j with j < g (two permlane swaps, no LDS).  The 16-lane swap of a with itself leaves
+// (a_0, a_0, a_2, a_2) and (a_1, a_1, a_3, a_3) over the four rows of 16 lanes; the
+// 32-lane swap of their sum leaves (a_0 + a_1) and (a_2 + a_3) in every row.
+__device__ __forceinline__ void quarter_scan(float a, int g, float& total, float& excl) {
   const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
-  const auto p0 = __builtin_amdgcn_permlane32_swap(r16[0], r16[0], false, false);
-  const auto p1 = __builtin_amdgcn_permlane32_swap(r16[1], r16[1], false, false);
-  H[0] = __uint_as_float(p0[0]);
-  H[1] = __uint_as_float(p1[0]);
-  H[2] = __uint_as_float(p0[1]);
-  H[3] = __uint_as_float(p1[1]);
+  const float e = __uint_as_float(r16[0]);
+  const float p = e + __uint_as_float(r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+  const float p01 = __uint_as_float(r32[0]), p23 = __uint_as_float(r32[1]);
+  total = p01 + p23;
+  excl = ((g & 1) ? e : 0.0f) + ((g & 2) ? p01 : 0.0f);
 }
 
 // One block of nval tokens starting at token t0 of a head, token by token, for a wave
@@ -316,7 +318,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
 
   for (int i = tid; i < Cfg::TOTAL / 16; i += NTHR) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
 
-  const float mult2 = gate_multiplier(A_log[h]) * kLog2e;
+  const float gmul = gate_multiplier(A_log[h]);
+  const float mult2 = gmul * kLog2e;
   constexpr unsigned kOOB = 0xFFFFFFF0u;       // a buffer offset past any range: reads zeros
   lds_barrier();                               // LDS cleared before any DMA lands
 
@@ -333,43 +336,34 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     const int pos = g;                          // quarter of the half: tokens 16*half + tq .. +3
     const int tq = 4 * pos;
     const bool kact = 2 * pair < K;
-    const bool precise = mult2 > 64.0f * kLog2e;
-    const float dtb0 = (kact && dt_bias) ? dt_bias[h * K + 2 * pair] : 0.0f;
-    const float dtb1 = (kact && dt_bias) ? dt_bias[h * K + 2 * pair + 1] : 0.0f;
+    const bool precise = gmul > 64.0f;
+    // dt_bias in log2 units: the gate is taken as -gmul softplus2(z log2(e) + dt_bias log2(e))
+    const float dtb0 = (kact && dt_bias) ? dt_bias[h * K + 2 * pair] * kLog2e : 0.0f;
+    const float dtb1 = (kact && dt_bias) ? dt_bias[h * K + 2 * pair + 1] * kLog2e : 0.0f;
     // per-head buffer resources: offsets past the head's T tokens read as 0
     const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(k + tb * K, (unsigned)(T * K * 2));
     const __amdgpu_buffer_rsrc_t rs_q = make_rsrc(q + tb * K, (unsigned)(T * K * 2));
     const __amdgpu_buffer_rsrc_t rs_z = make_rsrc(z + tb * K, (unsigned)(T * K * 2));
-    const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(v + tb * V, (unsigned)(T * V * 2));
-    const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(beta + tb, (unsigned)(T * 2));
 
-    // k, q, z of this lane's channel pair and four tokens (and beta, wave 0), loaded one
-    // block ahead into one of two register sets: the walk alternates between them, so a
-    // load never targets registers whose previous contents are still to be read.
+    // k, q, z of this lane's channel pair and four tokens, loaded one block ahead into one
+    // of two register sets: the walk alternates between them, so a load never targets
+    // registers whose previous contents are still to be read.  These 12 loads are the E
+    // waves' only memory operations, so the wait for a set leaves the next one in flight.
     struct Raw {
       uint32_t k[4], q[4], z[4];
-      bf16_t beta;
     };
+    // Byte offset of the lane's first row in block 0.  Lanes without a channel pair or
+    // without token rows (the second half when C = 16) start at 2^31, past any head's range
+    // (a head's rows, plus a block past its end, stay below 2^31 bytes): they read zeros.
+    const unsigned vbase = (kact && 16 * half < C) ? (unsigned)(((16 * half + tq) * K + 2 * pair) * 2) : 0x80000000u;
     auto load_qkz = [&](int b, Raw& r) __attribute__((always_inline)) {
+      const unsigned off = vbase + (unsigned)(b * C * K * 2);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int row = 16 * half + tq + t;
-        const unsigned off = (kact && row < C) ? (unsigned)(((b * C + row) * K + 2 * pair) * 2) : kOOB;
-        r.k[t] = buf_load_b32(rs_k, off);
-        r.q[t] = buf_load_b32(rs_q, off);
-        r.z[t] = buf_load_b32(rs_z, off);
+        r.k[t] = buf_load_b32(rs_k, off + t * K * 2);
+        r.q[t] = buf_load_b32(rs_q, off + t * K * 2);
+        r.z[t] = buf_load_b32(rs_z, off + t * K * 2);
       }
-    };
-    // value tile of block b into LDS (waves 0 .. NNT-1: 16 columns each, slot 2*row + half)
-    auto dma_v = [&](int b) __attribute__((always_inline)) {
-      if (wave < NNT) {
-        const int r = lane >> 1, c0 = 16 * wave + 8 * (lane & 1);
-        const unsigned off = (r < C && c0 < vcols) ? (unsigned)(((b * C + r) * V + v0 + c0) * 2) : kOOB;
-        dma16(rs_v, smem + Cfg::OFF_VRAW + (b % 3) * Cfg::VRAW_BUF + wave * 1024, off);
-      }
-    };
-    auto load_beta = [&](int tn, Raw& r) __attribute__((always_inline)) {
-      r.beta = tid < C ? __builtin_amdgcn_raw_buffer_load_b16(rs_b, (unsigned)((tn + tid) * 2), 0, 0) : (bf16_t)0;
     };
 
     auto e1 = [&](auto precise_tag, int b, const Raw& cur, Raw& nxt) __attribute__((always_inline)) {
@@ -383,7 +377,6 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       bf16_t* sKRT = reinterpret_cast<bf16_t*>(sb + Cfg::SET_KRT);
       float* sG0 = reinterpret_cast<float*>(sb + Cfg::SET_G0);
       float* sD0 = reinterpret_cast<float*>(sb + Cfg::SET_D0);
-      float* sBeta = reinterpret_cast<float*>(sb + Cfg::SET_BETA);
       Pair<bf16_t> rk[4], rq[4], rz[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -391,19 +384,13 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         rq[t].u = cur.q[t];
         rz[t].u = cur.z[t];
       }
-      const bf16_t rbeta = cur.beta;
-      // Issue this step's memory operations in a fixed order: beta of the next block
-      // (wave 0), the v DMA of this block, then the 12 loads of the next block, so that
-      // waiting for all but the last 12 completes the DMA and keeps the prefetch in flight.
-      // (past the last block these loads fall outside the head's range and read zeros)
-      if (wave == 0) load_beta(tn + C, nxt);
-      dma_v(b);
-      sched_fence();
+      // the next block's loads (past the last block they fall outside the head's range
+      // and read zeros)
       load_qkz(b + 1, nxt);
       sched_fence();
       // Tokens at or past nval (a partial last block, or rows 16..31 when C = 16) are
       // identity tokens: their k and q read as 0, and z = -inf makes their gate 0.
-      {
+      if (nval < 16 * half + 16) {
         const int lim = nval - (16 * half + tq);
 #pragma unroll
         for (int t = 0; t < 4; ++t) rz[t].u = t < lim ? rz[t].u : 0xFF80FF80u;
@@ -413,26 +400,20 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       float ax = 0.0f, ay = 0.0f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        ax += -mult2 * softplus_f(rz[t].x() + dtb0, PRECISE);
-        ay += -mult2 * softplus_f(rz[t].y() + dtb1, PRECISE);
+        ax = fmaf(-gmul, softplus2_f(fmaf(rz[t].x(), kLog2e, dtb0), PRECISE), ax);
+        ay = fmaf(-gmul, softplus2_f(fmaf(rz[t].y(), kLog2e, dtb1), PRECISE), ay);
         px[t] = ax;
         py[t] = ay;
       }
-      // the four quarter sums of this half, channel pair (lanes l16 + 16*j)
-      float Qx[4], Qy[4];
-      row_gather(ax, Qx);
-      row_gather(ay, Qy);
-      const float sumx = (Qx[0] + Qx[1]) + (Qx[2] + Qx[3]);
-      const float sumy = (Qy[0] + Qy[1]) + (Qy[2] + Qy[3]);
-      // exponent of token t relative to the reference: G_t - m = px[t] + off
-      float offx, offy;
-      if (half == 0) {
-        offx = pos == 0 ? -sumx : pos == 1 ? -(Qx[1] + Qx[2] + Qx[3]) : pos == 2 ? -(Qx[2] + Qx[3]) : -Qx[3];
-        offy = pos == 0 ? -sumy : pos == 1 ? -(Qy[1] + Qy[2] + Qy[3]) : pos == 2 ? -(Qy[2] + Qy[3]) : -Qy[3];
-      } else {
-        offx = pos == 0 ? 0.0f : pos == 1 ? Qx[0] : pos == 2 ? Qx[0] + Qx[1] : Qx[0] + Qx[1] + Qx[2];
-        offy = pos == 0 ? 0.0f : pos == 1 ? Qy[0] : pos == 2 ? Qy[0] + Qy[1] : Qy[0] + Qy[1] + Qy[2];
-      }
+      // Quarter sums of this half for the lane's channel pair (lanes l16 + 16j, j = 0..3):
+      // the sum over the half, and the sum over the quarters before the lane's own.
+      float sumx, sumy, exx, exy;
+      quarter_scan(ax, g, sumx, exx);
+      quarter_scan(ay, g, sumy, exy);
+      // exponent of token t relative to the reference: G_t - m = px[t] + off (the first
+      // half counts back from the reference, the second forward from it)
+      const float offx = half == 0 ? exx - sumx : exx;
+      const float offy = half == 0 ? exy - sumy : exy;
       if (kact) {
         const int c = 2 * pair;
         const int pc = perm32(c);              // c, c+1 are adjacent in perm32 order
@@ -445,10 +426,9 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           const int j = 16 * half + tq + t;
           krx[t] = kx * Rx;
           kry[t] = ky * Ry;
-          // KE is stored negated and QE with the read scale folded in (the V stage then
-          // needs neither a sign flip of v nor a scaling of o)
+          // KE is stored negated (the V stage then needs no sign flip of v)
           store2<bf16_t>(sKE + j * LD_TK + pc, -kx * Lx, -ky * Ly);
-          store2<bf16_t>(sQE + j * LD_TK + pc, scale * (qx * Lx), scale * (qy * Ly));
+          store2<bf16_t>(sQE + j * LD_TK + pc, qx * Lx, qy * Ly);
           store2<bf16_t>(sKR + j * LD_TK + pc, krx[t], kry[t]);
         }
         // K R^T rows c, c+1: this lane's four tokens in one 8-byte store each
@@ -471,25 +451,17 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           }
         }
       }
-      if (wave == 0 && tid < CD) sBeta[tid] = tid < nval ? bf2f(rbeta) : 0.0f;
       const unsigned long long bal = __ballot(kact && fminf(sumx, sumy) < -thresh);
       if (lane == 0) sFlag[(b % 3) * Cfg::NE + wave] = bal != 0ull;
     };
 
     Raw ra, rb;
-    ra.beta = rb.beta = 0;
-    if (nck > 0) {
-      if (wave == 0) load_beta(0, ra);
-      load_qkz(0, ra);
-    }
+    if (nck > 0) load_qkz(0, ra);
     auto estep = [&](int s, const Raw& cur, Raw& nxt) __attribute__((always_inline)) {
       const int b = s + 2;
       if (b < nck) {
         if (precise) e1(std::true_type{}, b, cur, nxt);
         else e1(std::false_type{}, b, cur, nxt);
-        // v rows of block b (and beta of block b+1) in LDS / registers before the barrier;
-        // the 12 loads of block b+1 may stay in flight
-        wait_vm_but12();
       }
       lds_barrier();
     };
@@ -501,9 +473,29 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     // ================================================================ W waves
     __builtin_amdgcn_s_setprio(2);             // issue ahead of the E waves (see the V waves)
     const int ww = wave - (Cfg::NE + Cfg::NV);
-    auto wstage = [&](int b) __attribute__((always_inline)) {
+    // The W waves also stage the next blocks' inputs that are not per channel pair: the v
+    // tile (waves 0 .. NNT-1 of the stage, 16 columns each, slot 2*row + half) and beta.
+    // Each W wave loads beta of the rows its tiles scale (tokens 16*I + l16); the last one
+    // loads all of the block's tokens and writes them to LDS for the V waves.  Both are
+    // issued after the wave's last LDS read of a step and waited for at the start of the
+    // next one, so their latency hides behind the barrier (an LDS DMA in flight would make
+    // every LDS read wait for it).  Tokens past the head's range read as 0.
+    const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(v + tb * V, (unsigned)(T * V * 2));
+    const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(beta + tb, (unsigned)(T * 2));
+    const int btok = ww == Cfg::NW - 1 ? lane : (ww == 0 ? 0 : 16) + l16;
+    auto load_beta = [&](int b) __attribute__((always_inline)) {
+      const unsigned off = btok < C ? (unsigned)((b * C + btok) * 2) : kOOB;
+      return __builtin_amdgcn_raw_buffer_load_b16(rs_b, off, 0, 0);
+    };
+    auto dma_v = [&](int b) __attribute__((always_inline)) {
+      if (ww < NNT) {
+        const int r = lane >> 1, c0 = 16 * ww + 8 * (lane & 1);
+        const unsigned off = (r < C && c0 < vcols) ? (unsigned)(((b * C + r) * V + v0 + c0) * 2) : kOOB;
+        dma16(rs_v, smem + Cfg::OFF_VRAW + (b % 3) * Cfg::VRAW_BUF + ww * 1024, off);
+      }
+    };
+    auto wstage = [&](int b, float rbeta) __attribute__((always_inline)) {
       char* sb = set_base(b);
-      const float* sBeta = reinterpret_cast<const float*>(sb + Cfg::SET_BETA);
       const bf16_t* sKE = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KE);
       const bf16_t* sQE = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_QE);
       const bf16_t* sKR = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KR);
@@ -534,11 +526,11 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
 #pragma unroll
         for (int r = 0; r < 4; ++r) vals[r] = (isA ? j0 + r < i : j0 + r <= i) ? acc[r] : 0.0f;
         if (isA && I == J) {                   // diagonal block: fp32 for the inverse
-          const float bi = -sBeta[i];          // (the tile is -A: KE is stored negated)
+          const float bi = -rbeta;             // beta of row i (the tile is -A: KE is stored negated)
           *reinterpret_cast<floatx4*>(sA + i * LD_A + j0) =
               floatx4{bi * vals[0], bi * vals[1], bi * vals[2], bi * vals[3]};
         } else if (isA) {                      // A_10: bf16, negated, for V
-          const float nb = sBeta[i];           // (the tile is -A_10)
+          const float nb = rbeta;              // (the tile is -A_10)
           store4_bf16(sA10 + l16 * LD_CT + perm32(j0), nb * vals[0], nb * vals[1], nb * vals[2], nb * vals[3]);
         } else {
           store4_bf16(sP + i * LD_CT + perm32(j0), vals[0], vals[1], vals[2], vals[3]);
@@ -642,9 +634,18 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         }
       }
     };
+    bf16_t wbeta = 0;                          // beta of block b, this lane's token
+    if (nck > 0) wbeta = load_beta(0);
     for (int s = -2; s < nck; ++s) {
       const int b = s + 1;
-      if (b >= 0 && b < nck && !slow_of(b)) wstage(b);
+      wait_vm();                               // beta of block b, v of block b+1
+      if (b >= 0 && b < nck) {
+        if (!slow_of(b)) wstage(b, bf2f(wbeta));
+        if (ww == Cfg::NW - 1 && lane < CD)
+          reinterpret_cast<float*>(set_base(b) + Cfg::SET_BETA)[lane] = bf2f(wbeta);
+      }
+      if (b + 1 < nck) wbeta = load_beta(b + 1);
+      if (s + 2 < nck) dma_v(s + 2);
       lds_barrier();
     }
   } else {
@@ -707,7 +708,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         // batches are sized so that the state and the live operands fit the register budget
         // of a 16-wave workgroup).
         // (A) Y = V - KE S~ (accumulated as V + (-KE) S~: KE is stored negated) and
-        // o^T = S~^T QE^T (+ U^T P^T below; QE and P carry the read scale), over the key
+        // o^T = S~^T QE^T (+ U^T P^T below; the read scale is applied at the store), over the key
         // depth in rounds of at most two 32-deep slices.  o is computed transposed: ln
         // holds token 16I + ll, value columns 16vw + 4g..+3.
         floatx4 Y[2], oT[NB];
@@ -794,7 +795,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
 #pragma unroll
           for (int I = 0; I < NB; ++I) {
             const int i = 16 * I + ll;
-            const u32x2 d = {pack_bf16x2(oT[I][0], oT[I][1]), pack_bf16x2(oT[I][2], oT[I][3])};
+            const u32x2 d = {pack_bf16x2(scale * oT[I][0], scale * oT[I][1]),
+                             pack_bf16x2(scale * oT[I][2], scale * oT[I][3])};
             if (i < nval && c0 < vcols)
               __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, (unsigned)(((t0c + i) * V + v0 + c0) * 2), 0, 0);
           }

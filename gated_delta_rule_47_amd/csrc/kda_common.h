@@ -60,6 +60,18 @@ __device__ __forceinline__ float softplus_f(float x, bool precise) {
   return fmaxf(x, 0.0f) + l;
 }
 
+// The same in log2 units: for x2 = x log2(e), softplus(x) log2(e) = max(x2, 0) + log2(1 + 2^-|x2|).
+__device__ __forceinline__ float softplus2_f(float x2, bool precise) {
+  float y = fast_exp2(-fabsf(x2));
+  float u = 1.0f + y;
+  float l = fast_log2(u);
+  if (precise) {
+    float d = u - 1.0f;
+    l = (d == 0.0f) ? y * kLog2e : l * (y * fast_rcp(d));
+  }
+  return fmaxf(x2, 0.0f) + l;
+}
+
 // ------------------------------------------------------------------ MFMA fragments
 // One wave computes a 16x16 fp32 tile C += A(16 x KS) * B(KS x 16) per instruction.
 // Operands live in LDS "depth-contiguous": A as [row][depth], B as [col][depth].

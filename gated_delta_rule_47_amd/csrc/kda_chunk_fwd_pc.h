@@ -4,7 +4,8 @@
 // walks the sequence in blocks of C <= 32 tokens.  The work of a block b splits into
 // three stages, each done by its own waves:
 //   E (waves 0-7):   the gate and block-local decay scans and the decay-weighted
-//                    operands KE, QE, KR (and KR^T); wave e covers one 16-token half of
+//                    operands KE, QE, KR (V reads KR^T from KR with transposing LDS
+//                    reads); wave e covers one 16-token half of
 //                    the block and 32 key channels, from q, k, z loaded straight into
 //                    registers one block ahead;
 //   V (waves 8-11):  the state-dependent part, each wave owning 16 value columns and all
@@ -80,19 +81,19 @@ struct PcCfg {
   static constexpr int LD_CT = CD + 8;                // [channel|token][token] bf16
   static constexpr int LD_A = CD + 4;                 // [token][token] fp32
   static constexpr int SZ_TK = CD * LD_TK * 2;
-  static constexpr int SZ_KT = KD * LD_CT * 2;
   static constexpr int SZ_TT = CD * LD_CT * 2;
-  // E outputs of one block (triple-buffered): KE, QE, KR, KR^T, G0, D0, beta, and
-  // F = D0 * G0 of the next block (written with the next block)
+  // E outputs of one block (triple-buffered): KE, QE, KR, G0, D0, beta, and F = D0 * G0 of
+  // the next block (written with the next block).  A block that takes the token path
+  // parks the state of the V waves in its set meanwhile, so a set holds at least that.
   static constexpr int SET_KE = 0;
   static constexpr int SET_QE = SET_KE + SZ_TK;
   static constexpr int SET_KR = SET_QE + SZ_TK;
-  static constexpr int SET_KRT = SET_KR + SZ_TK;
-  static constexpr int SET_G0 = SET_KRT + SZ_KT;
+  static constexpr int SET_G0 = SET_KR + SZ_TK;
   static constexpr int SET_D0 = SET_G0 + KD * 4;
   static constexpr int SET_F = SET_D0 + KD * 4;
   static constexpr int SET_BETA = SET_F + KD * 4;
-  static constexpr int SET_BYTES = SET_BETA + CD * 4;
+  static constexpr int PARK_BYTES = NV * NMT * 256 * 4;
+  static constexpr int SET_BYTES = round_up(SET_BETA + CD * 4 > PARK_BYTES ? SET_BETA + CD * 4 : PARK_BYTES, 16);
   // W outputs of one block (double-buffered): P, T (T_00 and T_11, zero elsewhere),
   // -A_10 (columns 0..15, zero in 16..31)
   static constexpr int WO_P = 0;
@@ -128,6 +129,24 @@ __device__ __forceinline__ constexpr int perm32(int x) {
 // = index d0+4g.., slots 4..7 = index d0+16+4g.. -- the accumulator-compatible order.
 __device__ __forceinline__ short8 lds_frag(const bf16_t* base, int ld, int row0, int d0, int lane) {
   return *reinterpret_cast<const short8*>(base + (row0 + (lane & 15)) * ld + d0 + 8 * (lane >> 4));
+}
+
+// The same fragment for the transpose of a [contraction index][row] tile whose columns
+// are stored in perm32 order (as the [token][channel] tiles are): rows [row0, row0+16)
+// (row0 a multiple of 16) are columns of the tile, the 32 contraction indices d0.. its
+// rows, in the natural order.  Two transposing reads: in each group of 16 lanes, lane
+// 4r + m reads row (d0 + 4g + r) (then d0 + 16 + 4g + r) at the four columns of rows
+// row0 + 4m..+3, which perm32 keeps adjacent, and lane j of the group receives the
+// column of row row0 + j of the four rows.
+__device__ __forceinline__ short8 lds_frag_tr(const bf16_t* base, int ld, int row0, int d0, int lane) {
+  typedef short short4v __attribute__((ext_vector_type(4)));
+  const int g = lane >> 4, r = (lane >> 2) & 3, m = lane & 3;
+  const bf16_t* p = base + (d0 + 4 * g + r) * ld + perm32(row0) + 8 * m;
+  const short4v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4v*)(__attribute__((address_space(3))) const void*)p);
+  const short4v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4v*)(__attribute__((address_space(3))) const void*)(p + 16 * ld));
+  return short8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 // Operand built from two accumulator tiles (depth rows 0..15 and 16..31).
@@ -277,11 +296,12 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   int* sFlag = reinterpret_cast<int*>(smem + Cfg::OFF_FLAG);   // [block % 3][E wave]
   // Buffer offsets of block b, passed through an empty asm so that the compiler keeps them
   // as one uniform term and folds each tile's constant offset into its LDS instructions.
-  auto set_base = [&](int b) __attribute__((always_inline)) {
-    int off = __builtin_amdgcn_readfirstlane((b % 3) * Cfg::SET_BYTES);
+  auto set_at = [&](int slot) __attribute__((always_inline)) {
+    int off = __builtin_amdgcn_readfirstlane(slot * Cfg::SET_BYTES);
     asm volatile("" : "+s"(off));
     return smem + Cfg::OFF_SET + off;
   };
+  auto set_base = [&](int b) __attribute__((always_inline)) { return set_at(b % 3); };
   auto wo_base = [&](int b) __attribute__((always_inline)) {
     int off = __builtin_amdgcn_readfirstlane((b & 1) * Cfg::WO_BYTES);
     asm volatile("" : "+s"(off));
@@ -355,26 +375,29 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     // Byte offset of the lane's first row in block 0.  Lanes without a channel pair or
     // without token rows (the second half when C = 16) start at 2^31, past any head's range
     // (a head's rows, plus a block past its end, stay below 2^31 bytes): they read zeros.
-    const unsigned vbase = (kact && 16 * half < C) ? (unsigned)(((16 * half + tq) * K + 2 * pair) * 2) : 0x80000000u;
+    const int rowb = (KD >= 64 ? KD : K) * 2;  // bytes per token row (K = KD unless KD = 32)
+    const unsigned vbase = (kact && 16 * half < C) ? (unsigned)((16 * half + tq) * rowb + 4 * pair) : 0x80000000u;
+    const int dpoff = kact ? 8 * pair : 0;     // this lane's channel pair in a per-channel fp32 array
     auto load_qkz = [&](int b, Raw& r) __attribute__((always_inline)) {
-      const unsigned off = vbase + (unsigned)(b * C * K * 2);
+      unsigned off = vbase + (unsigned)(b * C * rowb);
+      asm volatile("" : "+v"(off));            // one register; the row steps become immediates
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        r.k[t] = buf_load_b32(rs_k, off + t * K * 2);
-        r.q[t] = buf_load_b32(rs_q, off + t * K * 2);
-        r.z[t] = buf_load_b32(rs_z, off + t * K * 2);
+        r.k[t] = buf_load_b32(rs_k, off + t * rowb);
+        r.q[t] = buf_load_b32(rs_q, off + t * rowb);
+        r.z[t] = buf_load_b32(rs_z, off + t * rowb);
       }
     };
 
-    auto e1 = [&](auto precise_tag, int b, const Raw& cur, Raw& nxt) __attribute__((always_inline)) {
+    // e1 handles block b, whose buffers sit in slot sl = b % 3 (slp = (b - 1) % 3)
+    auto e1 = [&](auto precise_tag, int b, int sl, int slp, const Raw& cur, Raw& nxt) __attribute__((always_inline)) {
       constexpr bool PRECISE = decltype(precise_tag)::value;
       const int tn = b * C;
       const int nval = min(C, T - tn);
-      char* sb = set_base(b);
+      char* sb = set_at(sl);
       bf16_t* sKE = reinterpret_cast<bf16_t*>(sb + Cfg::SET_KE);
       bf16_t* sQE = reinterpret_cast<bf16_t*>(sb + Cfg::SET_QE);
       bf16_t* sKR = reinterpret_cast<bf16_t*>(sb + Cfg::SET_KR);
-      bf16_t* sKRT = reinterpret_cast<bf16_t*>(sb + Cfg::SET_KRT);
       float* sG0 = reinterpret_cast<float*>(sb + Cfg::SET_G0);
       float* sD0 = reinterpret_cast<float*>(sb + Cfg::SET_D0);
       Pair<bf16_t> rk[4], rq[4], rz[4];
@@ -388,6 +411,10 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       // and read zeros)
       load_qkz(b + 1, nxt);
       sched_fence();
+      // D0 of the previous block, for its F (first half; written a step ago).  Read first
+      // and used before this step's first LDS write, so that the wait for it is for it
+      // alone; its registers stay reserved to the end of the step (see below).
+      const float2 dprev = *reinterpret_cast<const float2*>(set_at(slp) + Cfg::SET_D0 + dpoff);
       // Tokens at or past nval (a partial last block, or rows 16..31 when C = 16) are
       // identity tokens: their k and q read as 0, and z = -inf makes their gate 0.
       if (nval < 16 * half + 16) {
@@ -414,60 +441,64 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       // half counts back from the reference, the second forward from it)
       const float offx = half == 0 ? exx - sumx : exx;
       const float offy = half == 0 ? exy - sumy : exy;
+      // first half: G0 = 2^m, and F = D0 G0 of the previous block
+      float2 g0 = float2{0.0f, 0.0f}, fp = float2{0.0f, 0.0f};
+      if (half == 0) {
+        g0 = float2{fast_exp2(sumx), fast_exp2(sumy)};
+        fp = float2{dprev.x * g0.x, dprev.y * g0.y};
+      }
+      const unsigned long long bal = __ballot(kact && fminf(sumx, sumy) < -thresh);
+      if (lane == 0) sFlag[sl * Cfg::NE + wave] = bal != 0ull;
+      const int c = 2 * pair;
+      if (half == 0 && kact && g == 0) {
+        *reinterpret_cast<float2*>(sG0 + c) = g0;
+        if (b > 0) *reinterpret_cast<float2*>(set_at(slp) + Cfg::SET_F + 4 * c) = fp;
+      }
       if (kact) {
-        const int c = 2 * pair;
         const int pc = perm32(c);              // c, c+1 are adjacent in perm32 order
-        float krx[4], kry[4];
+        float lx3 = 0.0f, ly3 = 0.0f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const float ex = px[t] + offx, ey = py[t] + offy;
           const float Lx = fast_exp2(ex), Ly = fast_exp2(ey), Rx = fast_exp2(-ex), Ry = fast_exp2(-ey);
           const float kx = rk[t].x(), ky = rk[t].y(), qx = rq[t].x(), qy = rq[t].y();
           const int j = 16 * half + tq + t;
-          krx[t] = kx * Rx;
-          kry[t] = ky * Ry;
           // KE is stored negated (the V stage then needs no sign flip of v)
           store2<bf16_t>(sKE + j * LD_TK + pc, -kx * Lx, -ky * Ly);
           store2<bf16_t>(sQE + j * LD_TK + pc, qx * Lx, qy * Ly);
-          store2<bf16_t>(sKR + j * LD_TK + pc, krx[t], kry[t]);
-        }
-        // K R^T rows c, c+1: this lane's four tokens in one 8-byte store each
-        *reinterpret_cast<uint2*>(sKRT + c * LD_CT + perm32(16 * half + tq)) =
-            uint2{pack_bf16x2(krx[0], krx[1]), pack_bf16x2(krx[2], krx[3])};
-        *reinterpret_cast<uint2*>(sKRT + (c + 1) * LD_CT + perm32(16 * half + tq)) =
-            uint2{pack_bf16x2(kry[0], kry[1]), pack_bf16x2(kry[2], kry[3])};
-        if (g == 0) {
-          const float2 f = float2{fast_exp2(sumx), fast_exp2(sumy)};
-          if (half == 0) {
-            // G0 = 2^m, and F = D0 G0 of the previous block (its D0 was written a step ago)
-            *reinterpret_cast<float2*>(sG0 + c) = f;
-            if (b > 0) {
-              char* sp = set_base(b - 1);
-              const float2 dp = *reinterpret_cast<const float2*>(sp + Cfg::SET_D0 + 4 * c);
-              *reinterpret_cast<float2*>(sp + Cfg::SET_F + 4 * c) = float2{dp.x * f.x, dp.y * f.y};
-            }
-          } else {
-            *reinterpret_cast<float2*>(sD0 + c) = f;   // D0 = 2^(G_last - m)
+          store2<bf16_t>(sKR + j * LD_TK + pc, kx * Rx, ky * Ry);
+          if (t == 3) {
+            lx3 = Lx;
+            ly3 = Ly;
           }
         }
+        // D0 = 2^(G_last - m): the second half's last token, whose L it is
+        if (half == 1 && g == 3) *reinterpret_cast<float2*>(sD0 + c) = float2{lx3, ly3};
       }
-      const unsigned long long bal = __ballot(kact && fminf(sumx, sumy) < -thresh);
-      if (lane == 0) sFlag[(b % 3) * Cfg::NE + wave] = bal != 0ull;
+      // (the second half never uses the D0 it read: without this, its registers could be
+      // reused while the read is in flight, and the write would first wait for every LDS
+      // operation of the step; the barrier waits for them anyway)
+      asm volatile("" ::"v"(dprev.x), "v"(dprev.y));
     };
 
     Raw ra, rb;
     if (nck > 0) load_qkz(0, ra);
-    auto estep = [&](int s, const Raw& cur, Raw& nxt) __attribute__((always_inline)) {
+    auto estep = [&](int s, int sl, int slp, const Raw& cur, Raw& nxt) __attribute__((always_inline)) {
       const int b = s + 2;
       if (b < nck) {
-        if (precise) e1(std::true_type{}, b, cur, nxt);
-        else e1(std::false_type{}, b, cur, nxt);
+        if (precise) e1(std::true_type{}, b, sl, slp, cur, nxt);
+        else e1(std::false_type{}, b, sl, slp, cur, nxt);
       }
       lds_barrier();
     };
+    int sl = 0, slp = 2;                       // slots of blocks s + 2 and s + 1
     for (int s = -2; s < nck; s += 2) {        // two steps per iteration: block s+2 from ra, s+3 from rb
-      estep(s, ra, rb);
-      if (s + 1 < nck) estep(s + 1, rb, ra);
+      estep(s, sl, slp, ra, rb);
+      slp = sl;
+      sl = __builtin_amdgcn_readfirstlane(sl == 2 ? 0 : sl + 1);
+      if (s + 1 < nck) estep(s + 1, sl, slp, rb, ra);
+      slp = sl;
+      sl = __builtin_amdgcn_readfirstlane(sl == 2 ? 0 : sl + 1);
     }
   } else if (wave >= Cfg::NE + Cfg::NV) {
     // ================================================================ W waves
@@ -694,7 +725,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       char* sb = set_base(b);
       const bf16_t* sKE = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KE);
       const bf16_t* sQE = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_QE);
-      const bf16_t* sKRT = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KRT);
+      const bf16_t* sKR = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KR);
       const float* sBeta = reinterpret_cast<const float*>(sb + Cfg::SET_BETA);
       char* wb = wo_base(b);
       const bf16_t* sP = reinterpret_cast<const bf16_t*>(wb + Cfg::WO_P);
@@ -771,7 +802,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
 #pragma unroll
           for (int I = 0; I < NB; ++I) oT[I] = mfma_bf16(ub, fp[I], oT[I]);
         }
-        // (D) S' = diag(F) (S~ + KR^T U), F = D0 G0' (next block scaled) or D0
+        // (D) S' = diag(F) (S~ + KR^T U), F = D0 G0' (next block scaled) or D0; KR^T
+        // comes from the [token][channel] KR tile through transposing reads
         sched_fence();
         const bool next_fast = b + 1 < nck && !any_flag(nf0, nf1);
         const float* sF = reinterpret_cast<const float*>(sb + (next_fast ? Cfg::SET_F : Cfg::SET_D0));
@@ -783,7 +815,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           floatx4 fs[NM];
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
-            fk[m] = lds_frag(sKRT, LD_CT, 16 * (hd * NM + m), 0, ln);
+            fk[m] = lds_frag_tr(sKR, LD_TK, 16 * (hd * NM + m), 0, ln);
             fs[m] = *reinterpret_cast<const floatx4*>(sF + 16 * (hd * NM + m) + 4 * lg);
           }
           sched_fence();

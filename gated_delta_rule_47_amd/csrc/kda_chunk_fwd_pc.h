@@ -180,6 +180,20 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, unsig
 // Wait until this wave's outstanding vector-memory operations (its DMAs, loads and
 // stores) have completed.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Two 4-byte LDS writes in one instruction, a at byte offset OFF0 from lds and b at OFF1
+// (multiples of 4 below 1024).  Written as asm so that the pairing is exactly this one; the
+// compiler does not count it among the wave's LDS operations, so the writer waits for
+// them itself (s_waitcnt lgkmcnt(0) in asm) before its next barrier.
+template <int OFF0, int OFF1>
+__device__ __forceinline__ void lds_write2_b32(const void* lds, uint32_t a, uint32_t b) {
+  static_assert(OFF0 % 4 == 0 && OFF1 % 4 == 0 && OFF0 / 4 < 256 && OFF1 / 4 < 256, "ds_write2_b32 offsets");
+  const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds;
+  asm volatile("ds_write2_b32 %0, %1, %2 offset0:%3 offset1:%4" ::"v"(addr), "v"(a), "v"(b), "i"(OFF0 / 4),
+               "i"(OFF1 / 4)
+               : "memory");
+}
+__device__ __forceinline__ void lds_wait_asm() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Wait until this wave's outstanding LDS operations have completed.
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
@@ -355,7 +369,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     const int pair = 16 * cw + l16;            // key-channel pair
     const int pos = g;                          // quarter of the half: tokens 16*half + tq .. +3
     const int tq = 4 * pos;
-    const bool kact = 2 * pair < K;
+    const bool kact = KD == 128 || 2 * pair < K;  // (K = KD = 128: every pair is a channel pair)
     const bool precise = gmul > 64.0f;
     // dt_bias in log2 units: the gate is taken as -gmul softplus2(z log2(e) + dt_bias log2(e))
     const float dtb0 = (kact && dt_bias) ? dt_bias[h * K + 2 * pair] * kLog2e : 0.0f;
@@ -378,6 +392,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     const int rowb = (KD >= 64 ? KD : K) * 2;  // bytes per token row (K = KD unless KD = 32)
     const unsigned vbase = (kact && 16 * half < C) ? (unsigned)((16 * half + tq) * rowb + 4 * pair) : 0x80000000u;
     const int dpoff = kact ? 8 * pair : 0;     // this lane's channel pair in a per-channel fp32 array
+    // element offset of the lane's first token row and channel pair in a [token][channel] tile
+    const int rowoff = (16 * half + tq) * LD_TK + perm32(2 * pair);
     auto load_qkz = [&](int b, Raw& r) __attribute__((always_inline)) {
       unsigned off = vbase + (unsigned)(b * C * rowb);
       asm volatile("" : "+v"(off));            // one register; the row steps become immediates
@@ -455,23 +471,32 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         if (b > 0) *reinterpret_cast<float2*>(set_at(slp) + Cfg::SET_F + 4 * c) = fp;
       }
       if (kact) {
-        const int pc = perm32(c);              // c, c+1 are adjacent in perm32 order
         float lx3 = 0.0f, ly3 = 0.0f;
+        uint32_t wke[4], wqe[4], wkr[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const float ex = px[t] + offx, ey = py[t] + offy;
           const float Lx = fast_exp2(ex), Ly = fast_exp2(ey), Rx = fast_exp2(-ex), Ry = fast_exp2(-ey);
           const float kx = rk[t].x(), ky = rk[t].y(), qx = rq[t].x(), qy = rq[t].y();
-          const int j = 16 * half + tq + t;
-          // KE is stored negated (the V stage then needs no sign flip of v)
-          store2<bf16_t>(sKE + j * LD_TK + pc, -kx * Lx, -ky * Ly);
-          store2<bf16_t>(sQE + j * LD_TK + pc, qx * Lx, qy * Ly);
-          store2<bf16_t>(sKR + j * LD_TK + pc, kx * Rx, ky * Ry);
+          wke[t] = pack_bf16x2(-kx * Lx, -ky * Ly);   // KE is stored negated (V then needs no sign flip of v)
+          wqe[t] = pack_bf16x2(qx * Lx, qy * Ly);
+          wkr[t] = pack_bf16x2(kx * Rx, ky * Ry);
           if (t == 3) {
             lx3 = Lx;
             ly3 = Ly;
           }
         }
+        // Rows t and t+2 in one instruction: the 64 bytes a group of 16 lanes writes to each
+        // of the two rows then fall on distinct LDS banks (rows t and t+1, 288 bytes apart,
+        // would share 8 of their 16 banks), and the lanes of groups g and g+1 (rows 4 apart)
+        // cover all 64 banks once.
+        constexpr int R1 = LD_TK * 2, R2 = 2 * R1, R3 = 3 * R1;   // row offsets in bytes
+        lds_write2_b32<0, R2>(sKE + rowoff, wke[0], wke[2]);
+        lds_write2_b32<R1, R3>(sKE + rowoff, wke[1], wke[3]);
+        lds_write2_b32<0, R2>(sQE + rowoff, wqe[0], wqe[2]);
+        lds_write2_b32<R1, R3>(sQE + rowoff, wqe[1], wqe[3]);
+        lds_write2_b32<0, R2>(sKR + rowoff, wkr[0], wkr[2]);
+        lds_write2_b32<R1, R3>(sKR + rowoff, wkr[1], wkr[3]);
         // D0 = 2^(G_last - m): the second half's last token, whose L it is
         if (half == 1 && g == 3) *reinterpret_cast<float2*>(sD0 + c) = float2{lx3, ly3};
       }
@@ -479,6 +504,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       // reused while the read is in flight, and the write would first wait for every LDS
       // operation of the step; the barrier waits for them anyway)
       asm volatile("" ::"v"(dprev.x), "v"(dprev.y));
+      lds_wait_asm();                          // the asm writes above, before the barrier
     };
 
     Raw ra, rb;
@@ -732,8 +758,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       const bf16_t* sT = reinterpret_cast<const bf16_t*>(wb + Cfg::WO_T);
       const bf16_t* sA10 = reinterpret_cast<const bf16_t*>(wb + Cfg::WO_A10);
       // staged values of this wave's 16 columns: slot 2*row + (column / 8)
-      const bf16_t* sV = reinterpret_cast<const bf16_t*>(smem + Cfg::OFF_VRAW + (b % 3) * Cfg::VRAW_BUF + vw * 1024) +
-                         (ll >> 3) * 8 + (ll & 7);
+      // staged values of this wave's 16 columns: row-major, 16 columns (32 bytes) per token
+      const bf16_t* sV = reinterpret_cast<const bf16_t*>(smem + Cfg::OFF_VRAW + (b % 3) * Cfg::VRAW_BUF + vw * 1024);
       if constexpr (FAST) {
         // Four phases, each loading its LDS operands as one batch before its MFMAs (the
         // batches are sized so that the state and the live operands fit the register budget
@@ -744,14 +770,14 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         // holds token 16I + ll, value columns 16vw + 4g..+3.
         floatx4 Y[2], oT[NB];
         {
-          bf16_t vv[NB][4];
-#pragma unroll
-          for (int I = 0; I < NB; ++I)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) vv[I][r] = sV[(16 * I + 4 * lg + r) * 16];
+          // column ll of tokens 16I + 4lg .. +3, one transposing read per I
+          typedef short short4v __attribute__((ext_vector_type(4)));
+          const bf16_t* pv = sV + (4 * lg + ((ln >> 2) & 3)) * 16 + 4 * (ln & 3);
 #pragma unroll
           for (int I = 0; I < NB; ++I) {
-            Y[I] = floatx4{bf2f(vv[I][0]), bf2f(vv[I][1]), bf2f(vv[I][2]), bf2f(vv[I][3])};
+            const short4v vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4v*)(__attribute__((address_space(3))) const void*)(pv + 256 * I));
+            Y[I] = floatx4{bf2f((bf16_t)vv[0]), bf2f((bf16_t)vv[1]), bf2f((bf16_t)vv[2]), bf2f((bf16_t)vv[3])};
             oT[I] = zero4();
           }
         }

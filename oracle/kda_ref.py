@@ -286,6 +286,37 @@ def _step_adjoint(dS, S_prev, S_t, q_t, k_t, v_t, a_t, b_t, do_t, scale):
     return a_t[..., :, None] * dSd, (dq_t, dk_t, dv_t, dg_t, dbeta_t)
 
 
+def sigmoid(x):
+    """1 / (1 + e^-x) = exp(-softplus(-x)): the derivative of softplus, overflow-free."""
+    return np.exp(-softplus(-np.asarray(x, dtype=np.float64)))
+
+
+def gate_adjoint(z, A_log, dt_bias, dg):
+    """Reverse mode of gate() for a cotangent dg on g  [fix, "Fix 1 -- decay form"].
+
+    With x = z + dt_bias and m = exp(clamp(A_log, -10, 20)), g = -m * softplus(x):
+      dz         = -m * sigmoid(x) * dg        (softplus' = sigmoid)
+      d dt_bias  = dz summed over batch and time                  (H, K)
+      dA_log     = (dg * g) summed over batch, time and channel,   (H,)
+                   where A_log lies in [-10, 20]; 0 outside, where the clamp
+                   holds the multiplier constant (at the two bounds the closed
+                   interval passes the gradient).
+    Returns (dz, dA_log, d_dt_bias), float64.  Steps written out one by one.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    dg = np.asarray(dg, dtype=np.float64)
+    A_log = np.asarray(A_log, dtype=np.float64)
+    a = np.clip(A_log, A_LOG_MIN, A_LOG_MAX)
+    m = np.exp(a)[None, :, None, None]
+    x = z + (np.asarray(dt_bias, dtype=np.float64)[None, :, None, :] if dt_bias is not None else 0.0)
+    g = -m * softplus(x)
+    dz = -m * sigmoid(x) * dg
+    inside = (A_log >= A_LOG_MIN) & (A_log <= A_LOG_MAX)
+    dA_log = np.where(inside, np.sum(dg * g, axis=(0, 2, 3)), 0.0)
+    d_dt_bias = np.sum(dz, axis=(0, 2))
+    return dz, dA_log, d_dt_bias
+
+
 def loss(q, k, v, g, beta, state_in, d_o, d_state_out=None, scale=None):
     """L = sum(o * d_o) + sum(S_T * d_state_out) through recurrent(); for FD checks."""
     o, S = recurrent(q, k, v, g, beta, state_in, scale)

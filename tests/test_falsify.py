@@ -129,3 +129,36 @@ def test_adjoint_mutant_fails_fd(monkeypatch):
     fd = R.fd_directional(fn, args["k"], d)
     an = float(np.sum(grads["dk"] * d))
     assert abs(fd - an) / max(abs(an), 1.0) > 1e-3
+
+
+def _gate_adjoint_sigmoid_of_z(z, A_log, dt_bias, dg):
+    # slope taken at z instead of z + dt_bias (a dropped term)
+    z = np.asarray(z, dtype=np.float64)
+    m = np.exp(np.clip(np.asarray(A_log, dtype=np.float64), R.A_LOG_MIN, R.A_LOG_MAX))[None, :, None, None]
+    x = z + np.asarray(dt_bias, dtype=np.float64)[None, :, None, :]
+    dz = -m * R.sigmoid(z) * dg
+    dA = np.sum(dg * (-m * R.softplus(x)), axis=(0, 2, 3))
+    return dz, dA, np.sum(dz, axis=(0, 2))
+
+
+def _gate_adjoint_no_clamp_mask(z, A_log, dt_bias, dg):
+    # the clamp ignored: A_log outside [-10, 20] still receives a gradient
+    dz, _, ddb = R.__dict__["_gate_adjoint_real"](z, A_log, dt_bias, dg)
+    m = np.exp(np.clip(np.asarray(A_log, dtype=np.float64), R.A_LOG_MIN, R.A_LOG_MAX))[None, :, None, None]
+    x = np.asarray(z, dtype=np.float64) + np.asarray(dt_bias, dtype=np.float64)[None, :, None, :]
+    return dz, np.sum(dg * (-m * R.softplus(x)), axis=(0, 2, 3)), ddb
+
+
+@pytest.mark.parametrize("mutant", [_gate_adjoint_sigmoid_of_z, _gate_adjoint_no_clamp_mask])
+def test_gate_adjoint_mutants_fail_pins(monkeypatch, mutant):
+    import test_oracle_adjoint as TA
+    monkeypatch.setattr(R, "_gate_adjoint_real", R.gate_adjoint, raising=False)
+    monkeypatch.setattr(R, "gate_adjoint", mutant)
+    failed = 0
+    for fn, args in ((TA.test_gate_adjoint_matches_central_differences, ("z",)),
+                     (TA.test_gate_adjoint_closed_forms, ())):
+        try:
+            fn(*args)
+        except AssertionError:
+            failed += 1
+    assert failed >= 1

@@ -89,3 +89,86 @@ def test_two_chunk_gradients_differ_from_one_chunk():
     a1["beta"] = args["beta"][:, :, :16]
     g1 = R.adjoint(*(a1[n] for n in ("q", "k", "v", "g", "beta", "state_in")), d_o[:, :, :16])
     assert R.rel_err(g2["dk"][:, :, :16], g1["dk"]) > 1e-3
+
+
+# ---------------------------------------------------------------------------- gate adjoint
+def _gate_inputs(seed=3, B=2, H=3, T=5, K=4):
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((B, H, T, K)) * 2.0
+    A_log = np.array([-1.5, 0.3, 1.1])[:H]
+    dt_bias = rng.standard_normal((H, K)) * 0.5
+    dg = rng.standard_normal((B, H, T, K))
+    return z, A_log, dt_bias, dg
+
+
+@pytest.mark.parametrize("wrt", ["z", "A_log", "dt_bias"])
+def test_gate_adjoint_matches_central_differences(wrt):
+    """dz, dA_log, d dt_bias against central differences of L = sum(dg * g) through
+    the pinned gate() (the softplus-outside form of the decay page)."""
+    z, A_log, dt_bias, dg = _gate_inputs()
+    dz, dA, ddb = R.gate_adjoint(z, A_log, dt_bias, dg)
+    vals = dict(z=z, A_log=A_log, dt_bias=dt_bias)
+    grads = dict(z=dz, A_log=dA, dt_bias=ddb)
+    d = np.random.default_rng(11).standard_normal(np.shape(vals[wrt]))
+
+    def fn(x):
+        a = dict(vals)
+        a[wrt] = x
+        return float(np.sum(dg * R.gate(a["z"], a["A_log"], a["dt_bias"])[0]))
+
+    fd = R.fd_directional(fn, vals[wrt], d)
+    an = float(np.sum(grads[wrt] * d))
+    assert abs(fd - an) / max(abs(an), 1.0) < BAR, (wrt, fd, an)
+
+
+def test_gate_adjoint_closed_forms():
+    """At x = z + dt_bias = 0 the softplus slope is 1/2: dz = -exp(A_log) dg / 2.  A
+    multiplier clamped at either bound passes no gradient to A_log (central
+    differences there are exactly 0), and without dt_bias the bias gradient is
+    still the per-channel sum of dz."""
+    z, A_log, dt_bias, dg = _gate_inputs()
+    zc = -np.broadcast_to(dt_bias[None, :, None, :], z.shape).copy()
+    dz, _, _ = R.gate_adjoint(zc, A_log, dt_bias, dg)
+    want = -np.exp(A_log)[None, :, None, None] * dg / 2.0
+    assert np.allclose(dz, want, rtol=1e-14, atol=0.0)
+
+    A_out = np.array([-12.0, 25.0, 0.5])
+    _, dA, _ = R.gate_adjoint(z, A_out, dt_bias, dg)
+    assert dA[0] == 0.0 and dA[1] == 0.0 and dA[2] != 0.0
+    for h in (0, 1):
+        e = np.zeros(3)
+        e[h] = 1.0
+        fd = R.fd_directional(lambda a: float(np.sum(dg * R.gate(z, a, dt_bias)[0])), A_out, e)
+        assert fd == 0.0
+
+    dz0, _, ddb0 = R.gate_adjoint(z, A_log, None, dg)
+    assert np.allclose(ddb0, dz0.sum(axis=(0, 2)), rtol=1e-14)
+
+
+def test_gate_adjoint_composes_with_the_recurrence_adjoint():
+    """End to end: d/dz of L = sum(o * d_o) through gate() and the token recurrence
+    equals gate_adjoint applied to the recurrence adjoint's dg (central differences
+    of the whole forward)."""
+    wl = ks.WORKLOADS["tiny"].with_(T=12, K=4, V=4, H=2)
+    x = ks.generate(wl)
+    q, k, v, beta = (x[n].astype(np.float64) for n in ("q", "k", "v", "beta"))
+    S0 = x["state_in"].astype(np.float64)
+    z, A_log, dt_bias = x["z"].astype(np.float64), x["A_log"], x["dt_bias"]
+    d_o = np.random.default_rng(5).standard_normal(v.shape)
+    g, _ = R.gate(z, A_log, dt_bias)
+    dg = R.adjoint(q, k, v, g, beta, S0, d_o)["dg"]
+    dz, dA, ddb = R.gate_adjoint(z, A_log, dt_bias, dg)
+    rng = np.random.default_rng(17)
+    for name, val, grad in (("z", z, dz), ("A_log", np.asarray(A_log, np.float64), dA),
+                            ("dt_bias", np.asarray(dt_bias, np.float64), ddb)):
+        d = rng.standard_normal(val.shape)
+
+        def fn(xv, name=name):
+            a = dict(z=z, A_log=A_log, dt_bias=dt_bias)
+            a[name] = xv
+            gg, _ = R.gate(a["z"], a["A_log"], a["dt_bias"])
+            return R.loss(q, k, v, gg, beta, S0, d_o)
+
+        fd = R.fd_directional(fn, val, d)
+        an = float(np.sum(grad * d))
+        assert abs(fd - an) / max(abs(an), 1.0) < BAR, (name, fd, an)

@@ -184,3 +184,27 @@ def chunk_bwd(q, k, v, z, A_log, dt_bias, beta, state_in, d_o, d_state_out=None,
           _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, T, K, V, _dtype_code(q),
           _stream(dev))
     return out
+
+
+def gate_bwd_workspace_bytes(B, H, T, K) -> int:
+    return int(_lib.load().kda_gate_bwd_workspace_bytes(B, H, T, K))
+
+
+def gate_bwd(z, A_log, dt_bias, dg, want_dz=True, workspace=None, dz_out=None):
+    """Adjoint of gate() for a cotangent dg on g: returns (dz or None, dA_log (H,),
+    d_dt_bias (H, K)), float32.  dz_out may be dg itself (computed in place)."""
+    B, H, T, K = z.shape
+    _check_f32("A_log", A_log, (H,))
+    _check_f32("dt_bias", dt_bias, (H, K))
+    _check_f32("dg", dg, (B, H, T, K))
+    dev = z.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    dz = (dz_out if dz_out is not None else torch.empty((B, H, T, K), **f32)) if want_dz else None
+    dA = torch.empty((H,), **f32)
+    ddb = torch.empty((H, K), **f32)
+    need = gate_bwd_workspace_bytes(B, H, T, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _call("kda_gate_bwd", _ptr(z), _ptr(A_log), _ptr(dt_bias), _ptr(dg), _ptr(dz), _ptr(dA), _ptr(ddb),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, T, K, _dtype_code(z), _stream(dev))
+    return dz, dA, ddb

@@ -10,9 +10,10 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 KDA_OK = 0
 KDA_F32 = 0
 KDA_BF16 = 1
-COUNTER_NAMES = ("gate", "chunk_fwd", "recurrent_step", "chunk_bwd", "rejected")
+COUNTER_NAMES = ("gate", "chunk_fwd", "recurrent_step", "chunk_bwd", "rejected", "gate_bwd")
 EXPORTED = ("kda_read_scale", "kda_gate", "kda_chunk_fwd", "kda_recurrent_step",
-            "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_status_string", "kda_get_counters")
+            "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_gate_bwd_workspace_bytes", "kda_gate_bwd",
+            "kda_status_string", "kda_get_counters")
 
 _lib = None
 
@@ -29,6 +30,8 @@ _PROTOS = {
     "kda_chunk_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "kda_chunk_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz,
                            _i, _i, _i, _i, _i, _i, _p]),
+    "kda_gate_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "kda_gate_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _sz, _i, _i, _i, _i, _i, _p]),
     "kda_status_string": (ctypes.c_char_p, [_i]),
     "kda_get_counters": (_i, [ctypes.POINTER(ctypes.c_ulonglong), _i]),
 }

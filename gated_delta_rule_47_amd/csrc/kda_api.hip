@@ -231,4 +231,38 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z, co
   return KDA_OK;
 }
 
+size_t kda_gate_bwd_workspace_bytes(int B, int H, int T, int K) { return gate_bwd_workspace_bytes(B, H, T, K); }
+
+int kda_gate_bwd(const void* z, const float* A_log, const float* dt_bias, const float* dg, float* dz, float* dA_log,
+                 float* d_dt_bias, void* workspace, size_t workspace_bytes, int B, int H, int T, int K, int dtype,
+                 void* stream) {
+  if (!A_log || (!dz && !dA_log && !d_dt_bias) || (T != 0 && (!z || !dg))) return reject(KDA_ERR_NULL);
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return reject(KDA_ERR_DTYPE);
+  if (B < 1 || H < 1 || T < 0 || K < 1) return reject(KDA_ERR_SHAPE);
+  const size_t need = gate_bwd_workspace_bytes(B, H, T, K);
+  if (need && (!workspace || workspace_bytes < need)) return reject(KDA_ERR_WORKSPACE);
+  const size_t n = (size_t)B * H * T * K;
+  struct Buf { const void* p; size_t n; };
+  const Buf ins[] = {{z, n * esize(dtype)}, {A_log, (size_t)H * 4}, {dt_bias, (size_t)H * K * 4}, {workspace, need}};
+  const Buf outs[] = {{dz, n * 4}, {dA_log, (size_t)H * 4}, {d_dt_bias, (size_t)H * K * 4}};
+  for (const Buf& a : outs) {
+    for (const Buf& b : ins)
+      if (overlap(a.p, a.n, b.p, b.n)) return reject(KDA_ERR_ALIAS);
+    for (const Buf& b : outs)
+      if (&a != &b && overlap(a.p, a.n, b.p, b.n)) return reject(KDA_ERR_ALIAS);
+  }
+  // dz may be dg itself (each element is read before it is written, by the same thread),
+  // but no other output may touch dg
+  if ((dz != dg && overlap(dz, n * 4, dg, n * 4)) || overlap(dA_log, (size_t)H * 4, dg, n * 4) ||
+      overlap(d_dt_bias, (size_t)H * K * 4, dg, n * 4))
+    return reject(KDA_ERR_ALIAS);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dtype == KDA_BF16
+                     ? launch_gate_bwd<bf16_t>(z, A_log, dt_bias, dg, dz, dA_log, d_dt_bias, workspace, B, H, T, K, s)
+                     : launch_gate_bwd<float>(z, A_log, dt_bias, dg, dz, dA_log, d_dt_bias, workspace, B, H, T, K, s);
+  if (e != hipSuccess) return reject(KDA_ERR_HIP);
+  g_counters[KDA_COUNTER_GATE_BWD].fetch_add(1, std::memory_order_relaxed);
+  return KDA_OK;
+}
+
 }  // extern "C"

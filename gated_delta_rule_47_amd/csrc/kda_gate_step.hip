@@ -33,6 +33,95 @@ __global__ void __launch_bounds__(256) gate_kernel(const Tin* __restrict__ z, co
   }
 }
 
+// Reverse of the gate for a cotangent dg on g.  With x = z + dt_bias and
+// m = exp(clamp(A_log)):  dz = -m sigmoid(x) dg  (the slope of softplus is the sigmoid);
+// d dt_bias[h][c] = dz summed over batch and time; dA_log[h] = dg g summed over batch,
+// time and channel where A_log lies in the closed clamp interval, else 0.
+// Pass 1 (elementwise, HBM-bound): one workgroup per (batch, head, tile of
+// kGateBwdTile tokens) writes dz and the tile's per-channel sums of dz and dg g to the
+// workspace; consecutive lanes take consecutive channels of a token row.  Pass 2: one
+// workgroup per head adds the tiles' sums in a fixed order, so the parameter gradients
+// do not depend on scheduling.
+constexpr int kGateBwdTile = 256;
+
+template <typename Tin>
+__global__ void __launch_bounds__(256) gate_bwd_tile_kernel(const Tin* __restrict__ z, const float* __restrict__ A_log,
+                                                            const float* __restrict__ dt_bias, const float* dg,
+                                                            float* dz, float* __restrict__ part, int H, int T, int K,
+                                                            int ntile) {
+  __shared__ float s_dz[256], s_gg[256];
+  const int wg = blockIdx.x;
+  const int bh = wg / ntile, tile = wg % ntile;
+  const int h = bh % H;
+  const int t0 = tile * kGateBwdTile, t1 = min(T, t0 + kGateBwdTile);
+  const float m = gate_multiplier(A_log[h]);
+  const int tid = threadIdx.x;
+  float* pw = part + (size_t)wg * 2 * K;
+  for (int cb = 0; cb < K; cb += 256) {
+    const int KC = min(K - cb, 256);          // channels of this pass
+    const int rpp = 256 / KC;                 // token rows per pass
+    const int r = tid / KC, c = cb + tid % KC;
+    float sdz = 0.0f, sgg = 0.0f;
+    if (r < rpp) {
+      const float db = dt_bias ? dt_bias[h * K + c] : 0.0f;
+      for (int t = t0 + r; t < t1; t += rpp) {
+        const size_t idx = ((size_t)bh * T + t) * K + c;
+        const float x = to_f<Tin>(z[idx]) + db;
+        const float dgv = dg[idx];
+        const float g = -m * softplus_f(x, true);
+        const float sig = fast_rcp(1.0f + fast_exp2(-x * kLog2e));   // 0 as x -> -inf, 1 as x -> inf
+        const float d = -m * sig * dgv;
+        if (dz) dz[idx] = d;                   // (dz may be dg itself: read above, same thread)
+        sdz += d;
+        sgg += dgv * g;
+      }
+    }
+    s_dz[tid] = sdz;
+    s_gg[tid] = sgg;
+    __syncthreads();
+    if (tid < KC) {
+      float a = 0.0f, e = 0.0f;
+      for (int j = 0; j < rpp; ++j) {
+        a += s_dz[j * KC + tid];
+        e += s_gg[j * KC + tid];
+      }
+      pw[c] = a;
+      pw[K + c] = e;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void __launch_bounds__(256) gate_bwd_reduce_kernel(const float* __restrict__ part,
+                                                              const float* __restrict__ A_log, float* dA_log,
+                                                              float* d_dt_bias, int B, int H, int K, int ntile) {
+  __shared__ float s_red[256];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x;
+  float gg = 0.0f;
+  for (int c = tid; c < K; c += 256) {
+    float sdz = 0.0f, sgg = 0.0f;
+    for (int b = 0; b < B; ++b)
+      for (int tile = 0; tile < ntile; ++tile) {
+        const float* pw = part + ((size_t)(b * H + h) * ntile + tile) * 2 * K;
+        sdz += pw[c];
+        sgg += pw[K + c];
+      }
+    if (d_dt_bias) d_dt_bias[h * K + c] = sdz;
+    gg += sgg;
+  }
+  s_red[tid] = gg;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) s_red[tid] += s_red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0 && dA_log) {
+    const float a = A_log[h];
+    dA_log[h] = (a >= kALogMin && a <= kALogMax) ? s_red[0] : 0.0f;
+  }
+}
+
 template <typename Tin, int K, int VTS>
 __global__ void __launch_bounds__(256) step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                                                    const Tin* __restrict__ v, const Tin* __restrict__ z,
@@ -107,6 +196,35 @@ hipError_t launch_gate(const void* z, const float* A_log, const float* dt_bias, 
                      alpha, H, T, K, n);
   return hipGetLastError();
 }
+
+size_t gate_bwd_workspace_bytes(int B, int H, int T, int K) {
+  if (B < 1 || H < 1 || T < 0 || K < 1) return 0;
+  const size_t ntile = (size_t)(T + kGateBwdTile - 1) / kGateBwdTile;
+  return (size_t)B * H * ntile * 2 * K * sizeof(float);
+}
+
+template <typename Tin>
+hipError_t launch_gate_bwd(const void* z, const float* A_log, const float* dt_bias, const float* dg, float* dz,
+                           float* dA_log, float* d_dt_bias, void* workspace, int B, int H, int T, int K,
+                           hipStream_t s) {
+  const int ntile = (T + kGateBwdTile - 1) / kGateBwdTile;
+  float* part = reinterpret_cast<float*>(workspace);
+  if (ntile > 0) {
+    hipLaunchKernelGGL(gate_bwd_tile_kernel<Tin>, dim3((unsigned)(B * H * ntile)), dim3(256), 0, s, (const Tin*)z,
+                       A_log, dt_bias, dg, dz, part, H, T, K, ntile);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (dA_log || d_dt_bias)                    // (T = 0: both come out zero)
+    hipLaunchKernelGGL(gate_bwd_reduce_kernel, dim3((unsigned)H), dim3(256), 0, s, part, A_log, dA_log, d_dt_bias, B,
+                       H, K, ntile);
+  return hipGetLastError();
+}
+
+template hipError_t launch_gate_bwd<float>(const void*, const float*, const float*, const float*, float*, float*,
+                                           float*, void*, int, int, int, int, hipStream_t);
+template hipError_t launch_gate_bwd<bf16_t>(const void*, const float*, const float*, const float*, float*, float*,
+                                            float*, void*, int, int, int, int, hipStream_t);
 
 template <typename Tin, int K, int VTS>
 static hipError_t launch_step_kv(const void* q, const void* k, const void* v, const void* z, const float* A_log,

@@ -12,6 +12,13 @@ template <typename Tin>
 hipError_t launch_gate(const void* z, const float* A_log, const float* dt_bias, float* g, float* alpha, int B, int H,
                        int T, int K, hipStream_t s);
 
+// Gate adjoint: dz (nullable), dA_log and d_dt_bias (nullable) for a cotangent dg.
+size_t gate_bwd_workspace_bytes(int B, int H, int T, int K);
+template <typename Tin>
+hipError_t launch_gate_bwd(const void* z, const float* A_log, const float* dt_bias, const float* dg, float* dz,
+                           float* dA_log, float* d_dt_bias, void* workspace, int B, int H, int T, int K,
+                           hipStream_t s);
+
 template <typename Tin>
 hipError_t launch_step(const void* q, const void* k, const void* v, const void* z, const float* A_log,
                        const float* dt_bias, const void* beta, float* state, float scale, void* o, int B, int H,

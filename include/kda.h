@@ -133,6 +133,27 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z,
                   void* workspace, size_t workspace_bytes,
                   int B, int H, int T, int K, int V, int dtype, void* stream);
 
+/* Bytes of device workspace kda_gate_bwd needs for these sizes (0 when T = 0 or on
+ * bad sizes). */
+size_t kda_gate_bwd_workspace_bytes(int B, int H, int T, int K);
+
+/* Adjoint of kda_gate for a cotangent dg on g ("kdafix" page, "Fix 1 -- decay form",
+ * differentiated): with x = z + dt_bias and m = exp(clamp(A_log, -10, 20)),
+ *   dz         (B,H,T,K) f32 = -m * sigmoid(x) * dg        (NULL: not written)
+ *   dA_log     (H) f32 = sum over b, t, c of dg * g, or 0 where A_log lies outside
+ *              [-10, 20] (the clamp holds the multiplier constant there)   (NULL: not written)
+ *   d_dt_bias  (H,K) f32 = sum over b, t of dz  (also when dt_bias is NULL)  (NULL: not written)
+ * Inputs: z (B,H,T,K) in `dtype`, A_log (H) f32, dt_bias (H,K) f32 or NULL (= 0),
+ * dg (B,H,T,K) f32 (as kda_chunk_bwd returns it).  At least one output is needed.
+ * workspace: device buffer of at least kda_gate_bwd_workspace_bytes() (may be NULL
+ * when that is 0); contents on entry ignored.  dz may be dg itself (computed in
+ * place); no other overlap between outputs, inputs and workspace is allowed.  The
+ * parameter gradients are reduced in a fixed order (bitwise repeatable).  K >= 1. */
+int kda_gate_bwd(const void* z, const float* A_log, const float* dt_bias, const float* dg,
+                 float* dz, float* dA_log, float* d_dt_bias,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int H, int T, int K, int dtype, void* stream);
+
 /* Static string for a status code ("ok", "null pointer", ...). Never NULL. */
 const char* kda_status_string(int status);
 
@@ -140,12 +161,13 @@ const char* kda_status_string(int status);
  * Counters are process-wide and monotonic: calls accepted per entry point and
  * calls rejected with an error status (modelled on the page's dispatch counters,
  * "The fused KDA adjoint" page, section 6). */
-#define KDA_NUM_COUNTERS 5
+#define KDA_NUM_COUNTERS 6
 #define KDA_COUNTER_GATE 0
 #define KDA_COUNTER_CHUNK_FWD 1
 #define KDA_COUNTER_RECURRENT_STEP 2
 #define KDA_COUNTER_CHUNK_BWD 3
 #define KDA_COUNTER_REJECTED 4
+#define KDA_COUNTER_GATE_BWD 5
 int kda_get_counters(unsigned long long* out, int n);
 
 #ifdef __cplusplus

@@ -51,7 +51,7 @@ def test_status_strings_and_counters():
     assert lib.kda_status_string(-99) == b"unknown status"
     n = lib.kda_get_counters(None, 0)
     arr = (ctypes.c_ulonglong * n)()
-    assert lib.kda_get_counters(arr, n) == n == 5
+    assert lib.kda_get_counters(arr, n) == n == 6
 
 
 def test_workspace_bytes():
@@ -60,6 +60,10 @@ def test_workspace_bytes():
     assert lib.kda_chunk_bwd_workspace_bytes(1, 1, 32, 7, 8, 16) == 0
     assert lib.kda_chunk_bwd_workspace_bytes(1, 1, 32, 8, 8, 48) == 0
     assert lib.kda_chunk_bwd_workspace_bytes(0, 1, 32, 8, 8, 16) == 0
+    # gate adjoint: one (dz, dg*g) pair of per-channel sums per (b, h, 256-token tile)
+    assert lib.kda_gate_bwd_workspace_bytes(2, 3, 300, 8) == 2 * 3 * 2 * 2 * 8 * 4
+    assert lib.kda_gate_bwd_workspace_bytes(1, 1, 0, 8) == 0
+    assert lib.kda_gate_bwd_workspace_bytes(1, 1, 16, 0) == 0
 
 
 def _gpu_visible():
@@ -76,8 +80,8 @@ def test_argument_errors_before_launch():
     P = ctypes.c_void_p
     fake = [P(0x10000 * (i + 1)) for i in range(12)]
     q, k, v, z, A, dt, b, s_in, o, s_out = fake[:10]
-    rej0 = (ctypes.c_ulonglong * 5)()
-    lib.kda_get_counters(rej0, 5)
+    rej0 = (ctypes.c_ulonglong * 6)()
+    lib.kda_get_counters(rej0, 6)
     # null input
     assert lib.kda_chunk_fwd(None, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 8, 0, None) == -1
     # bad dtype
@@ -112,6 +116,18 @@ def test_argument_errors_before_launch():
     assert lib.kda_chunk_bwd(*args, g[0], 1 << 40, 1, 1, 16, 8, 8, 1, None) == -3
     assert lib.kda_chunk_bwd(*args, None, 0, 1, 1, 16, 8, 8, 0, None) == -7
     assert lib.kda_chunk_bwd(*args, g[0], 16, 1, 1, 16, 8, 8, 0, None) == -7
-    rej1 = (ctypes.c_ulonglong * 5)()
-    lib.kda_get_counters(rej1, 5)
-    assert rej1[4] - rej0[4] == 19 and list(rej1[:4]) == list(rej0[:4])
+    # gate adjoint: no output / null input, bad dtype, bad shape, workspace, aliasing
+    ws = fake[11]
+    assert lib.kda_gate_bwd(z, A, dt, g[0], None, None, None, ws, 1 << 20, 1, 1, 16, 8, 0, None) == -1
+    assert lib.kda_gate_bwd(None, A, dt, g[0], o, None, None, ws, 1 << 20, 1, 1, 16, 8, 0, None) == -1
+    assert lib.kda_gate_bwd(z, A, dt, g[0], o, None, None, ws, 1 << 20, 1, 1, 16, 8, 5, None) == -3
+    assert lib.kda_gate_bwd(z, A, dt, g[0], o, None, None, ws, 1 << 20, 1, 1, 16, 0, 0, None) == -2
+    assert lib.kda_gate_bwd(z, A, dt, g[0], o, None, None, None, 0, 1, 1, 16, 8, 0, None) == -7
+    assert lib.kda_gate_bwd(z, A, dt, g[0], o, None, None, ws, 4, 1, 1, 16, 8, 0, None) == -7
+    assert lib.kda_gate_bwd(z, A, dt, g[0], z, None, None, ws, 1 << 20, 1, 1, 16, 8, 0, None) == -5
+    assert lib.kda_gate_bwd(z, A, dt, g[0], o, dt, None, ws, 1 << 20, 1, 1, 16, 8, 0, None) == -5
+    assert lib.kda_gate_bwd(z, A, dt, g[0], P(g[0].value + 4), None, None, ws, 1 << 20, 1, 1, 16, 8, 0,
+                            None) == -5
+    rej1 = (ctypes.c_ulonglong * 6)()
+    lib.kda_get_counters(rej1, 6)
+    assert rej1[4] - rej0[4] == 28 and list(rej1[:4]) == list(rej0[:4]) and rej1[5] == rej0[5]

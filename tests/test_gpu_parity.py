@@ -257,3 +257,67 @@ def test_chunk_bwd_adjoint_workload_sampled_heads():
     for n in GRADS:
         got = np.stack([host(gr[n][b, h]) for b, h in heads])[None]
         _check(n, got, ref[n], 1e-4)
+
+
+# ----------------------------------------------------------------------------- gate adjoint
+GATE_BWD_CASES = [("f32", 2, 3, 300, 64), ("bf16", 2, 3, 300, 64), ("f32", 1, 2, 17, 24), ("f32", 1, 2, 0, 8),
+                  ("bf16", 1, 2, 513, 320)]
+
+
+def _gate_bwd_inputs(B, H, T, K, dtype, seed=23):
+    rng = np.random.default_rng(seed)
+    z = (rng.standard_normal((B, H, T, K)) * 4).astype(np.float32)
+    if T:
+        z[0, 0, 0, :8] = [-50, -20, -5, 0, 5, 20, 50, 1]
+    if dtype == "bf16":
+        z = ks.round_bf16(z)
+    A_log = np.array([-3.0, 25.0, 0.0][:H], dtype=np.float32)     # head 1 clamped: no dA_log
+    dt = (0.5 * rng.standard_normal((H, K))).astype(np.float32)
+    dg = rng.standard_normal((B, H, T, K)).astype(np.float32)
+    return z, A_log, dt, dg
+
+
+@pytest.mark.parametrize("dtype,B,H,T,K", GATE_BWD_CASES)
+def test_gate_bwd(dtype, B, H, T, K):
+    """dz, dA_log and d dt_bias against the oracle's gate adjoint: ragged token tiles,
+    K above one pass of 256 lanes, T = 0, a clamped multiplier, dz computed in place
+    over dg, and bitwise-repeatable parameter gradients."""
+    z, A_log, dt, dg = _gate_bwd_inputs(B, H, T, K, dtype)
+    zd = to_dev(z, torch.bfloat16 if dtype == "bf16" else torch.float32)
+    Ad, dtd, dgd = (to_dev(x, torch.float32) for x in (A_log, dt, dg))
+    dz, dA, ddb = kda.gate_bwd(zd, Ad, dtd, dgd)
+    dzr, dAr, ddbr = R.gate_adjoint(z, A_log, dt, dg)
+    say(dtype, B, H, T, K)
+    if T:
+        _check("dz", host(dz), dzr, 2e-6)
+        _check("dA_log", host(dA), dAr, 1e-4)
+        _check("d_dt_bias", host(ddb), ddbr, 1e-4)
+        if H > 1:
+            assert host(dA)[1] == 0.0
+    else:
+        assert np.all(host(dA) == 0.0) and np.all(host(ddb) == 0.0)
+    _, dA2, ddb2 = kda.gate_bwd(zd, Ad, dtd, dgd, want_dz=False)
+    assert torch.equal(dA, dA2) and torch.equal(ddb, ddb2)
+    if T:
+        dg_inplace = dgd.clone()
+        dzi, _, _ = kda.gate_bwd(zd, Ad, dtd, dg_inplace, dz_out=dg_inplace)
+        assert dzi.data_ptr() == dg_inplace.data_ptr()
+        assert torch.equal(dzi, dz)
+
+
+def test_gate_bwd_after_chunk_bwd_end_to_end():
+    """The training chain: the adjoint's dg fed to the gate adjoint gives dz, dA_log and
+    d dt_bias of sum(o * d_o); the oracle runs the same chain in f64."""
+    K, V, chunk, T = 8, 8, 16, 45
+    wl = ks.WORKLOADS["adjoint"].with_(B=2, H=2, K=K, V=V, chunk=chunk)
+    x = ks.generate(wl, T=T)
+    d = upload(wl, x)
+    gr = _bwd(d, chunk, None)
+    dz, dA, ddb = kda.gate_bwd(d["z"], d["A_log"], d["dt_bias"], gr["dg"])
+    heads = [(b, h) for b in range(2) for h in range(2)]
+    ref = _oracle_bwd(wl, x, heads, None)
+    dg_ref = ref["dg"].reshape(2, 2, T, K)
+    dzr, dAr, ddbr = R.gate_adjoint(x["z"], x["A_log"], x["dt_bias"], dg_ref)
+    _check("dz", host(dz), dzr, 1e-4)
+    _check("dA_log", host(dA), dAr, 1e-4)
+    _check("d_dt_bias", host(ddb), ddbr, 1e-4)

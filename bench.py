@@ -118,6 +118,40 @@ def traffic_from_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_
     print(json.dumps(out, indent=1))
 
 
+def decode_bench(B, steps, warmup, H=32, K=128, V=128):
+    """Decode step at one token per sequence: the state (B,H,K,V) fp32 is read and written
+    once, so the bound is HBM at 2*K*V*4 bytes per head plus the token's activations.
+    Prints one JSON line (not the headline metric)."""
+    import torch
+    import gated_delta_rule_47_amd as kda
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(7)
+    act = lambda *s: (torch.randn(*s, device=dev, generator=g) * 0.1).to(torch.bfloat16)
+    q, k, z, v = act(B, H, K), act(B, H, K), act(B, H, K), act(B, H, V)
+    beta = torch.rand(B, H, device=dev, generator=g).to(torch.bfloat16)
+    A_log = torch.zeros(H, device=dev)
+    dt_bias = torch.zeros(H, K, device=dev)
+    S = torch.randn(B, H, K, V, device=dev, generator=g) * 0.1
+    o = torch.empty(B, H, V, dtype=torch.bfloat16, device=dev)
+    for _ in range(warmup):
+        kda.recurrent_step(q, k, v, z, A_log, dt_bias, beta, S, out=o)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        kda.recurrent_step(q, k, v, z, A_log, dt_bias, beta, S, out=o)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    nbytes = B * H * (2 * K * V * 4 + (3 * K + 2 * V + 1) * 2)
+    print(json.dumps({"metric": "decode step state bandwidth (kda_recurrent_step)", "value": round(nbytes / us / 1e3, 1),
+                      "unit": "GB/s", "frac_of_8TBps": round(nbytes / us / 1e3 / 8000.0, 4), "us_per_step": round(us, 2),
+                      "bytes_per_step": nbytes, "steps": steps,
+                      "config": {"B": B, "H": H, "K": K, "V": V, "activations": "bf16", "state": "f32"},
+                      "note": "HIP events around the launches; includes launch gaps when the host is slower"}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +168,9 @@ def main():
                     help="write --traffic-json from rocprofv3 --pmc CSV directories of the kernel (FETCH_SIZE, "
                          "WRITE_SIZE) and of a --copy-calibration-mib run (same counters); no GPU work")
     ap.add_argument("--calibration-mib", type=int, default=1024, help="size of the calibration copy, MiB")
+    ap.add_argument("--decode-batch", type=int, default=0,
+                    help="instead of the benchmark, time the decode step (kda_recurrent_step) for this many "
+                         "sequences of H=32 heads, K=V=128, bf16 activations (--steps launches)")
     args = ap.parse_args()
     if args.traffic_from_pmc:
         traffic_from_pmc(*args.traffic_from_pmc, args.calibration_mib, args.workload, args.traffic_json)
@@ -147,6 +184,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": n, "launches": args.steps}))
+        return
+    if args.decode_batch:
+        decode_bench(args.decode_batch, args.steps, args.warmup)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (heads shard across GPUs "

@@ -158,6 +158,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="override the workload's chunk (16, 32 or 64) to compare block sizes; the default "
+                         "line uses the workload's own")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_long.json"),
                     help="HBM traffic per launch measured by rocprofv3 counters (if present)")
@@ -198,6 +201,8 @@ def main():
     import kda_synth as ks
 
     wl = ks.WORKLOADS[args.workload]
+    if args.chunk:
+        wl = wl.with_(chunk=args.chunk)
     if wl.adjoint:
         raise SystemExit("the benchmark times the forward; pick a forward workload")
     print("bench: generating %s (%s)" % (wl.name, wl.desc), file=sys.stderr, flush=True)

@@ -321,3 +321,20 @@ def test_gate_bwd_after_chunk_bwd_end_to_end():
     _check("dz", host(dz), dzr, 1e-4)
     _check("dA_log", host(dA), dAr, 1e-4)
     _check("d_dt_bias", host(ddb), ddbr, 1e-4)
+
+
+def test_gate_bwd_adjoint_workload_full_size():
+    """The gate adjoint at the adjoint workload's full size (2 x 16 heads x 8192 tokens,
+    K = 128, fp32): dz on sampled heads, the parameter gradients (sums over every token)
+    in full, against the oracle."""
+    wl = ks.WORKLOADS["adjoint"]
+    x = ks.generate(wl)
+    dg = np.random.default_rng(31).standard_normal((wl.B, wl.H, wl.T, wl.K)).astype(np.float32)
+    d = upload(wl, x)
+    dz, dA, ddb = kda.gate_bwd(d["z"], d["A_log"], d["dt_bias"], to_dev(dg, torch.float32))
+    torch.cuda.synchronize()
+    dzr, dAr, ddbr = R.gate_adjoint(x["z"], x["A_log"], x["dt_bias"], dg)
+    for b, h in [(0, 0), (1, 9)]:
+        _check("dz[%d,%d]" % (b, h), host(dz[b, h]), dzr[b, h], 2e-6)
+    _check("dA_log", host(dA), dAr, 1e-4)
+    _check("d_dt_bias", host(ddb), ddbr, 1e-4)

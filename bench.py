@@ -248,13 +248,14 @@ def main():
     if os.path.exists(args.traffic_json):
         try:
             tj = json.load(open(args.traffic_json))
-            if tj.get("workload") == wl.name and tj.get("kernel_source_sha256") == kernel_source_hash():
+            if (tj.get("workload") == wl.name and tj.get("kernel_source_sha256") == kernel_source_hash()
+                    and not args.chunk):
                 traffic = tj.get("bytes_per_launch")
         except Exception:
             traffic = None
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": KERNEL_NAME, "algorithmic_bytes_per_launch": nbytes,
+            "kernel": KERNEL_NAME.replace("32>", "%d>" % min(wl.chunk, 32)), "algorithmic_bytes_per_launch": nbytes,
             "avg_kernel_ms": round(avg_kernel_ms, 4), "min_kernel_ms": round(float(np.min(kern_ms)), 4)}
     cpu = None
     if not args.no_cpu_baseline:

@@ -338,3 +338,41 @@ def test_gate_bwd_adjoint_workload_full_size():
         _check("dz[%d,%d]" % (b, h), host(dz[b, h]), dzr[b, h], 2e-6)
     _check("dA_log", host(dA), dAr, 1e-4)
     _check("d_dt_bias", host(ddb), ddbr, 1e-4)
+
+
+# ----------------------------------------------------------------------------- K = V = 128, bf16, many heads
+def test_k128_saturated_gates_and_many_heads():
+    """K = V = 128 bf16 (two value-tile workgroups per head): token-path blocks mixed
+    with mild heads, more heads than the device has compute units, a ragged tail,
+    checked on heads spread over the whole grid."""
+    wl = ks.WORKLOADS["nano"].with_(B=2, H=80, K=128, V=128, chunk=64, a_log="uniform:-3,1", state="normal:0.1")
+    x = ks.generate(wl, T=45)
+    x["A_log"][3] = 20.0
+    x["z"][1, 3, 10:30] += 6.0
+    x["z"] = ks.round_bf16(x["z"])
+    d = upload(wl, x)
+    o, S = _fwd(d, 64)
+    heads = [(0, 0), (0, 3), (1, 3), (1, 47), (1, 48), (1, 79)]
+    o_ref, S_ref = oracle_heads(wl, x, heads)
+    og = np.stack([host(o[b, h]) for b, h in heads])[None]
+    Sg = np.stack([host(S[b, h]) for b, h in heads])[None]
+    _check("o", og, o_ref, TOL["bf16"])
+    _check("state", Sg, S_ref, TOL["bf16"])
+
+
+def test_k128_state_none_and_in_place_state():
+    wl = ks.WORKLOADS["nano"].with_(B=1, H=4, K=128, V=128, chunk=64, state="normal:0.1")
+    x = ks.generate(wl, T=97)
+    d = upload(wl, x)
+    o0, S0 = _fwd(d, 64, state_in=False)
+    x0 = dict(x)
+    x0["state_in"] = np.zeros_like(x["state_in"])
+    o_ref, S_ref = oracle_heads(wl, x0, [(0, h) for h in range(4)])
+    _check("o", host(o0).reshape(1, 4, 97, 128), o_ref, TOL["bf16"])
+    _check("state", host(S0).reshape(1, 4, 128, 128), S_ref, TOL["bf16"])
+    S_io = d["state_in"].clone()
+    o1 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["z"], d["A_log"], d["dt_bias"], d["beta"], S_io, chunk=64,
+                       state_out=S_io)[0]
+    o_ref1, S_ref1 = oracle_heads(wl, x, [(0, h) for h in range(4)])
+    _check("o", host(o1).reshape(1, 4, 97, 128), o_ref1, TOL["bf16"])
+    _check("state", host(S_io).reshape(1, 4, 128, 128), S_ref1, TOL["bf16"])

@@ -152,11 +152,74 @@ def decode_bench(B, steps, warmup, H=32, K=128, V=128):
                       "note": "HIP events around the launches; includes launch gaps when the host is slower"}))
 
 
+FP32_PEAK_TFLOPS = 157.3      # MI355X dense fp32 (matrix), published
+
+
+def forward_flops_per_head_token(K: int, V: int, C: int) -> float:
+    """Algorithmic flops of the chunked forward per head-token, counting triangular
+    products by their nonzero half: 6KV for the state (the decayed read W~S, the output
+    read Q~S and the update KR^T U), (C-1)K for the strictly-lower A, (C+1)(K+V) for the
+    lower scores P and their product with U, (C-1)(K+V) for forming w and u, and C^2/3
+    for the unit-triangular inverse."""
+    return 6 * K * V + (C - 1) * K + (C + 1) * (K + V) + (C - 1) * (K + V) + C * C / 3
+
+
+def adjoint_bench(steps, warmup):
+    """kda_chunk_bwd on the adjoint workload (B=2, H=16, T=8192, K=V=128, fp32, chunk 64).
+    One JSON line (not the headline metric): head-tokens/s and the fp32 matrix roofline,
+    with algorithmic flops = the forward's recomputation plus two products per forward
+    product (3x the forward's flops per head-token)."""
+    import torch
+    import gated_delta_rule_47_amd as kda
+    import kda_synth as ks
+    wl = ks.WORKLOADS["adjoint"]
+    x = ks.generate(wl)
+    dev = torch.device("cuda:0")
+    d = {n: torch.from_numpy(x[n]).to(dev) for n in ("q", "k", "v", "z", "beta", "A_log", "dt_bias", "state_in",
+                                                     "d_out")}
+    del x
+    ws = torch.empty(kda.chunk_bwd_workspace_bytes(wl.B, wl.H, wl.T, wl.K, wl.V, wl.chunk), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        return kda.chunk_bwd(d["q"], d["k"], d["v"], d["z"], d["A_log"], d["dt_bias"], d["beta"], d["state_in"],
+                             d["d_out"], chunk=wl.chunk, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        out = step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    if not all(torch.isfinite(t).all() for t in out.values()):
+        raise SystemExit("non-finite gradient")
+    ht = wl.B * wl.H * wl.T
+    flops = 3 * forward_flops_per_head_token(wl.K, wl.V, wl.chunk) * ht
+    nbytes = ht * ((3 * wl.K + 2 * wl.V + 1) + (3 * wl.K + wl.V + 1)) * 4 + 2 * wl.B * wl.H * wl.K * wl.V * 4
+    achieved = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({"metric": "KDA chunked adjoint head-tokens/s (kda_chunk_bwd)", "value": round(ht / (ms * 1e-3), 1),
+                      "unit": "tokens/s", "ms_per_step": round(ms, 3), "steps": steps, "warmup": warmup,
+                      "dtype": "f32", "data": "synthetic",
+                      "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "K": wl.K, "V": wl.V,
+                                 "chunk": wl.chunk},
+                      "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": FP32_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 5),
+                                   "algorithmic_flops_per_call": flops, "algorithmic_bytes_per_call": nbytes,
+                                   "note": "whole call (checkpointing forward, reverse walk, tile reduction), "
+                                           "HIP events on the launch stream"}}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed launches first: the GPU takes ~50 ms of load to reach its steady clock")
     ap.add_argument("--workload", default="long")
     ap.add_argument("--chunk", type=int, default=0,
                     help="override the workload's chunk (16, 32 or 64) to compare block sizes; the default "
@@ -174,6 +237,8 @@ def main():
     ap.add_argument("--decode-batch", type=int, default=0,
                     help="instead of the benchmark, time the decode step (kda_recurrent_step) for this many "
                          "sequences of H=32 heads, K=V=128, bf16 activations (--steps launches)")
+    ap.add_argument("--adjoint", action="store_true",
+                    help="instead of the benchmark, time kda_chunk_bwd on the adjoint workload (fp32)")
     args = ap.parse_args()
     if args.traffic_from_pmc:
         traffic_from_pmc(*args.traffic_from_pmc, args.calibration_mib, args.workload, args.traffic_json)
@@ -188,12 +253,15 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": n, "launches": args.steps}))
         return
+    if args.adjoint:
+        adjoint_bench(args.steps, min(args.warmup, 5))
+        return
     if args.decode_batch:
         decode_bench(args.decode_batch, args.steps, args.warmup)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (heads shard across GPUs "
-              "with no communication; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+              "with no communication). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -18,6 +18,8 @@ What the method computes (per batch b and head h, all in float64):
   gate        g = -exp(clamp(A_log_h, -10, 20)) * softplus(z + dt_bias_h)    [fix, Fix 1]
               alpha = exp(g) <= 1
   read scale  q_hat = scale * q, default scale = K**-0.5                    [fix, Fix 2]
+  scalar decay  one pre-activation per token and one bias per head: the same gate,
+              the same alpha on every key channel (gate_scalar, recurrent_scalar)
   recurrence  S' = diag(alpha_t) S_{t-1}
               S_t = S' + beta_t k_t (v_t - S'^T k_t)^T
               o_t = S_t^T q_hat_t
@@ -133,6 +135,29 @@ def recurrent_step(q_t, k_t, v_t, g_t, beta_t, state, scale=None):
     scale = read_scale(K) if scale is None else float(scale)
     S, o = _step(np.asarray(state, dtype=np.float64), q_t, k_t, v_t, np.exp(g_t), beta_t, scale)
     return o, S
+
+
+# ============================================================================ scalar-decay special case
+def gate_scalar(a, A_log, dt_bias=None):
+    """Scalar (per-head) decay: one gate pre-activation a per (b, h, t) and one bias per
+    head, so all key channels of a head decay by the same factor.  This is the released
+    gate [fix, "Fix 1 -- decay form"] with an input that is constant over the channels:
+    g_t = -exp(clamp(A_log_h, -10, 20)) * softplus(a_t + dt_bias_h).
+
+    a: (B,H,T); A_log: (H,); dt_bias: (H,) or None (zeros).  Returns (g, alpha), (B,H,T).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    db = np.zeros(a.shape[1]) if dt_bias is None else np.asarray(dt_bias, dtype=np.float64)
+    Al = np.clip(np.asarray(A_log, dtype=np.float64), A_LOG_MIN, A_LOG_MAX)
+    g = -np.exp(Al)[None, :, None] * softplus(a + db[None, :, None])
+    return g, np.exp(g)
+
+
+def recurrent_scalar(q, k, v, g, beta, state_in=None, scale=None):
+    """The token recurrence under a scalar decay g (B,H,T): alpha_t scales the whole state
+    before the delta read.  Defined as the KDA recurrence with g copied to every key channel."""
+    g = np.asarray(g, dtype=np.float64)
+    return recurrent(q, k, v, np.broadcast_to(g[..., None], np.shape(q)), beta, state_in, scale)
 
 
 # ============================================================================ chunked (WY) form

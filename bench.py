@@ -25,22 +25,25 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 METRIC = "KDA chunked-forward tokens/s (B·H·T/s) + % of roofline, H=32,K=V=128,T=16k"
+METRIC_SCALAR = "KDA chunked-forward tokens/s, scalar-decay gate (kda_chunk_fwd_scalar), H=32,K=V=128,T=16k"
 
 
-def algorithmic_bytes(wl) -> int:
+def algorithmic_bytes(wl, scalar_gate=False) -> int:
     """HBM bytes one kda_chunk_fwd call must move at minimum: read q, k, z, v, beta
     and the initial state once, write o and the final state once (A_log, dt_bias
-    are negligible but counted)."""
+    are negligible but counted).  With the scalar-decay gate, z is one value per
+    head-token and dt_bias one per head."""
     es = 2 if wl.dtype == "bf16" else 4
     ht = wl.B * wl.H * wl.T
-    acts = ht * (3 * wl.K + wl.V + 1) * es + ht * wl.V * es
+    zc = 1 if scalar_gate else wl.K
+    acts = ht * (2 * wl.K + zc + wl.V + 1) * es + ht * wl.V * es
     state = 2 * wl.B * wl.H * wl.K * wl.V * 4
-    params = wl.H * 4 + wl.H * wl.K * 4
+    params = wl.H * 4 + wl.H * zc * 4
     return acts + state + params
 
 
 KERNEL_SOURCES = ("kda_chunk_fwd_pc.h", "kda_common.h")
-KERNEL_NAME = "kda::chunk_fwd_pc_kernel<128,64,32>"
+KERNEL_NAME = "kda::chunk_fwd_pc_kernel<128,64,32,false>"
 
 
 def kernel_source_hash() -> str:
@@ -55,7 +58,7 @@ def kernel_source_hash() -> str:
 
 def _oracle_head(args):
     """CPU baseline worker: the f64 oracle's token recurrence on one head."""
-    wl_name, b, h = args
+    wl_name, b, h, scalar_gate = args
     os.environ.setdefault("OMP_NUM_THREADS", "1")
     import kda_synth as ks
     from oracle import kda_ref as R
@@ -63,19 +66,24 @@ def _oracle_head(args):
     A_log, dt_bias = ks.head_params(wl)
     sl = ks.head_slice(wl, b, h)
     t0 = time.time()
-    g, _ = R.gate(sl["z"][None, None], A_log[h:h + 1], dt_bias[h:h + 1])
-    R.recurrent(sl["q"][None, None], sl["k"][None, None], sl["v"][None, None], g, sl["beta"][None, None],
-                sl["state_in"][None, None])
+    if scalar_gate:
+        g, _ = R.gate_scalar(sl["z"][None, None, :, 0], A_log[h:h + 1], dt_bias[h:h + 1, 0])
+        R.recurrent_scalar(sl["q"][None, None], sl["k"][None, None], sl["v"][None, None], g, sl["beta"][None, None],
+                           sl["state_in"][None, None])
+    else:
+        g, _ = R.gate(sl["z"][None, None], A_log[h:h + 1], dt_bias[h:h + 1])
+        R.recurrent(sl["q"][None, None], sl["k"][None, None], sl["v"][None, None], g, sl["beta"][None, None],
+                    sl["state_in"][None, None])
     return t0, time.time()
 
 
-def cpu_baseline(wl, n_heads: int, workers: int) -> dict:
+def cpu_baseline(wl, n_heads: int, workers: int, scalar_gate: bool = False) -> dict:
     """The f64 oracle (gate + token recurrence) on n_heads whole heads, one per process:
     head-tokens per second of wall time from the first head's start to the last head's
     end (input generation excluded)."""
     heads = [(i // wl.H % wl.B, i % wl.H) for i in range(n_heads)]
     with ProcessPoolExecutor(workers) as ex:
-        spans = list(ex.map(_oracle_head, [(wl.name, b, h) for b, h in heads]))
+        spans = list(ex.map(_oracle_head, [(wl.name, b, h, scalar_gate) for b, h in heads]))
     wall = max(e for _, e in spans) - min(s for s, _ in spans)
     cpu = sum(e - s for s, e in spans)
     return {"value": n_heads * wl.T / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
@@ -237,6 +245,9 @@ def main():
     ap.add_argument("--decode-batch", type=int, default=0,
                     help="instead of the benchmark, time the decode step (kda_recurrent_step) for this many "
                          "sequences of H=32 heads, K=V=128, bf16 activations (--steps launches)")
+    ap.add_argument("--scalar-gate", action="store_true",
+                    help="time kda_chunk_fwd_scalar instead (one gate input per head-token: channel 0 of the "
+                         "workload's z, bias channel 0 of its dt_bias); a separate metric line")
     ap.add_argument("--adjoint", action="store_true",
                     help="instead of the benchmark, time kda_chunk_bwd on the adjoint workload (fp32)")
     args = ap.parse_args()
@@ -282,13 +293,18 @@ def main():
     dt_bias = torch.from_numpy(x["dt_bias"]).to(dev)
     state_in = torch.from_numpy(x["state_in"]).to(dev)
     del x
+    if args.scalar_gate:
+        d["z"] = d["z"][..., 0].contiguous()
+        dt_bias = dt_bias[:, 0].contiguous()
     o = torch.empty((wl.B, wl.H, wl.T, wl.V), dtype=dt, device=dev)
     state_out = torch.empty_like(state_in)
     scale = kda.read_scale(wl.K)
 
+    fwd = kda.chunk_fwd_scalar if args.scalar_gate else kda.chunk_fwd
+
     def step():
-        kda.chunk_fwd(d["q"], d["k"], d["v"], d["z"], A_log, dt_bias, d["beta"], state_in, scale=scale,
-                      chunk=wl.chunk, out=o, state_out=state_out)
+        fwd(d["q"], d["k"], d["v"], d["z"], A_log, dt_bias, d["beta"], state_in, scale=scale, chunk=wl.chunk, out=o,
+            state_out=state_out)
 
     for _ in range(args.warmup):
         step()
@@ -310,28 +326,29 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     avg_kernel_ms = float(np.mean(kern_ms))
     tokens = wl.B * wl.H * wl.T
-    nbytes = algorithmic_bytes(wl)
+    nbytes = algorithmic_bytes(wl, args.scalar_gate)
     achieved = nbytes / (avg_kernel_ms * 1e-3) / 1e9
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
             tj = json.load(open(args.traffic_json))
             if (tj.get("workload") == wl.name and tj.get("kernel_source_sha256") == kernel_source_hash()
-                    and not args.chunk):
+                    and not args.chunk and not args.scalar_gate):
                 traffic = tj.get("bytes_per_launch")
         except Exception:
             traffic = None
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": KERNEL_NAME.replace("32>", "%d>" % min(wl.chunk, 32)), "algorithmic_bytes_per_launch": nbytes,
+            "kernel": KERNEL_NAME.replace("32,false>", "%d,%s>" % (min(wl.chunk, 32), str(args.scalar_gate).lower())),
+            "algorithmic_bytes_per_launch": nbytes,
             "avg_kernel_ms": round(avg_kernel_ms, 4), "min_kernel_ms": round(float(np.min(kern_ms)), 4)}
     cpu = None
     if not args.no_cpu_baseline:
         workers = min(16, len(os.sched_getaffinity(0)))
         print("bench: CPU oracle baseline on %d heads" % workers, file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, n_heads=workers, workers=workers)
+        cpu = cpu_baseline(wl, n_heads=workers, workers=workers, scalar_gate=args.scalar_gate)
     out = {
-        "metric": METRIC, "value": round(tokens / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC_SCALAR if args.scalar_gate else METRIC, "value": round(tokens / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "K": wl.K, "V": wl.V, "chunk": wl.chunk,

@@ -17,7 +17,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["KdaError", "read_scale", "gate", "chunk_fwd", "recurrent_step", "chunk_bwd",
+__all__ = ["KdaError", "read_scale", "gate", "chunk_fwd", "chunk_fwd_scalar", "recurrent_step", "recurrent_step_scalar", "chunk_bwd",
            "chunk_bwd_workspace_bytes", "counters", "status_string", "library_path"]
 
 
@@ -99,10 +99,11 @@ def gate(z, A_log, dt_bias=None, want_alpha=True):
     return g, alpha
 
 
-def _check_acts(q, k, v, z, beta):
+def _check_acts(q, k, v, z, beta, scalar_gate=False):
     B, H, T, K = q.shape
     V = v.shape[-1]
-    for name, t, shape in (("k", k, (B, H, T, K)), ("z", z, (B, H, T, K)), ("v", v, (B, H, T, V)),
+    zshape = (B, H, T) if scalar_gate else (B, H, T, K)
+    for name, t, shape in (("k", k, (B, H, T, K)), ("z", z, zshape), ("v", v, (B, H, T, V)),
                            ("beta", beta, (B, H, T))):
         if tuple(t.shape) != shape:
             raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), shape))
@@ -115,9 +116,23 @@ def chunk_fwd(q, k, v, z, A_log, dt_bias, beta, state_in=None, scale=None, chunk
               output_state=True, out=None, state_out=None):
     """Chunked KDA forward.  Returns (o, state_out); state_out is None when
     output_state is False.  scale=None means K**-0.5."""
-    B, H, T, K, V = _check_acts(q, k, v, z, beta)
+    return _chunk_fwd("kda_chunk_fwd", q, k, v, z, A_log, dt_bias, beta, state_in, scale, chunk, output_state,
+                      out, state_out)
+
+
+def chunk_fwd_scalar(q, k, v, a, A_log, dt_bias, beta, state_in=None, scale=None, chunk=64,
+                     output_state=True, out=None, state_out=None):
+    """Chunked forward under a scalar decay: a (B,H,T) one gate input per token and
+    head, dt_bias (H,) or None.  Otherwise as chunk_fwd."""
+    return _chunk_fwd("kda_chunk_fwd_scalar", q, k, v, a, A_log, dt_bias, beta, state_in, scale, chunk,
+                      output_state, out, state_out)
+
+
+def _chunk_fwd(fn, q, k, v, z, A_log, dt_bias, beta, state_in, scale, chunk, output_state, out, state_out):
+    scalar_gate = fn == "kda_chunk_fwd_scalar"
+    B, H, T, K, V = _check_acts(q, k, v, z, beta, scalar_gate)
     _check_f32("A_log", A_log, (H,))
-    _check_f32("dt_bias", dt_bias, (H, K))
+    _check_f32("dt_bias", dt_bias, (H,) if scalar_gate else (H, K))
     _check_f32("state_in", state_in, (B, H, K, V))
     if scale is None:
         scale = read_scale(K)
@@ -126,7 +141,7 @@ def chunk_fwd(q, k, v, z, A_log, dt_bias, beta, state_in=None, scale=None, chunk
         state_out = torch.empty((B, H, K, V), dtype=torch.float32, device=q.device)
     if not output_state:
         state_out = None
-    _call("kda_chunk_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(dt_bias), _ptr(beta),
+    _call(fn, _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(dt_bias), _ptr(beta),
           _ptr(state_in), float(scale), int(chunk), _ptr(o), _ptr(state_out), B, H, T, K, V,
           _dtype_code(q), _stream(q.device))
     return o, state_out
@@ -135,20 +150,32 @@ def chunk_fwd(q, k, v, z, A_log, dt_bias, beta, state_in=None, scale=None, chunk
 def recurrent_step(q, k, v, z, A_log, dt_bias, beta, state, scale=None, out=None):
     """One decode token per (b,h): q,k,z (B,H,K), v (B,H,V), beta (B,H).  Updates
     `state` (B,H,K,V) float32 in place and returns o (B,H,V)."""
+    return _recurrent_step("kda_recurrent_step", q, k, v, z, A_log, dt_bias, beta, state, scale, out)
+
+
+def recurrent_step_scalar(q, k, v, a, A_log, dt_bias, beta, state, scale=None, out=None):
+    """Decode step under a scalar decay: a (B,H) one gate input per sequence and head,
+    dt_bias (H,) or None.  Otherwise as recurrent_step."""
+    return _recurrent_step("kda_recurrent_step_scalar", q, k, v, a, A_log, dt_bias, beta, state, scale, out)
+
+
+def _recurrent_step(fn, q, k, v, z, A_log, dt_bias, beta, state, scale, out):
+    scalar_gate = fn == "kda_recurrent_step_scalar"
     B, H, K = q.shape
     V = v.shape[-1]
-    for name, t, shape in (("k", k, (B, H, K)), ("z", z, (B, H, K)), ("v", v, (B, H, V)), ("beta", beta, (B, H))):
+    zshape = (B, H) if scalar_gate else (B, H, K)
+    for name, t, shape in (("k", k, (B, H, K)), ("z", z, zshape), ("v", v, (B, H, V)), ("beta", beta, (B, H))):
         if tuple(t.shape) != shape:
             raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), shape))
         if t.dtype != q.dtype:
             raise TypeError("%s has dtype %s, q has %s" % (name, t.dtype, q.dtype))
     _check_f32("A_log", A_log, (H,))
-    _check_f32("dt_bias", dt_bias, (H, K))
+    _check_f32("dt_bias", dt_bias, (H,) if scalar_gate else (H, K))
     _check_f32("state", state, (B, H, K, V))
     if scale is None:
         scale = read_scale(K)
     o = out if out is not None else torch.empty((B, H, V), dtype=q.dtype, device=q.device)
-    _call("kda_recurrent_step", _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(dt_bias), _ptr(beta),
+    _call(fn, _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(dt_bias), _ptr(beta),
           _ptr(state), float(scale), _ptr(o), B, H, K, V, _dtype_code(q), _stream(q.device))
     return o
 

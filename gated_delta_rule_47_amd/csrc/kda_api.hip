@@ -47,14 +47,14 @@ bool fwd_plan(bool bf16, int K, int V, int chunk, FwdPlan* p) {
 
 static hipError_t launch_fwd(bool bf16, const FwdPlan& p, const void* q, const void* k, const void* v, const void* z,
                              const float* A_log, const float* dt_bias, const void* beta, const float* state_in,
-                             float scale, void* o, float* state_out, int B, int H, int T, int K, int V,
+                             float scale, void* o, float* state_out, int B, int H, int T, int K, int V, int zc,
                              hipStream_t s) {
 #define KDA_FWD(TYPE, KD_)                                                                                    \
   return launch_chunk_fwd_kd<TYPE, KD_>(p.VT, p.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, o,     \
-                                         state_out, nullptr, B, H, T, K, V, s)
+                                         state_out, nullptr, B, H, T, K, V, zc, s)
 #define KDA_FWD_PC(KD_)                                                                                       \
   return launch_chunk_fwd_pc_kd<KD_>(p.VT, p.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, o, state_out, B, \
-                                     H, T, K, V, s)
+                                     H, T, K, V, zc, s)
   if (bf16) {
     switch (p.KD) {
       case 32: KDA_FWD_PC(32);
@@ -127,9 +127,14 @@ int kda_gate(const void* z, const float* A_log, const float* dt_bias, float* g_o
   return KDA_OK;
 }
 
-int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* z, const float* A_log,
-                  const float* dt_bias, const void* beta, const float* state_in, float scale, int chunk, void* o,
-                  float* state_out, int B, int H, int T, int K, int V, int dtype, void* stream) {
+}  // extern "C"
+
+// kda_chunk_fwd (zc = 1: z (B,H,T,K), dt_bias (H,K)) and kda_chunk_fwd_scalar (zc = 0:
+// z (B,H,T), dt_bias (H)): checks, then one launch.
+static int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* z, const float* A_log,
+                          const float* dt_bias, const void* beta, const float* state_in, float scale, int chunk,
+                          void* o, float* state_out, int B, int H, int T, int K, int V, int dtype, void* stream,
+                          int zc) {
   if (!A_log || (T != 0 && (!q || !k || !v || !z || !beta || !o))) return reject(KDA_ERR_NULL);
   if (dtype != KDA_F32 && dtype != KDA_BF16) return reject(KDA_ERR_DTYPE);
   if (B < 1 || H < 1 || T < 0 || !valid_dim(K) || !valid_dim(V)) return reject(KDA_ERR_SHAPE);
@@ -139,18 +144,21 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* z, co
   // reads of up to 64 tokens past T that the range check turns into zeros)
   if ((size_t)(T + 64) * (size_t)(K > V ? K : V) * es > 0x7fffffffu) return reject(KDA_ERR_SHAPE);
   const uintptr_t amask = 2 * es - 1;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)z) & amask) return reject(KDA_ERR_ALIGN);
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (zc ? (uintptr_t)z : 0)) & amask) return reject(KDA_ERR_ALIGN);
+  if ((uintptr_t)z & (es - 1)) return reject(KDA_ERR_ALIGN);
   const size_t nk = (size_t)B * H * T * K * es, nv = (size_t)B * H * T * V * es, nb = (size_t)B * H * T * es;
+  const size_t nz = zc ? nk : nb;
   const size_t ns = (size_t)B * H * K * V * 4;
-  const void* ins[] = {q, k, z};
+  const void* ins[] = {q, k};
   for (const void* p : ins)
     if (overlap(o, nv, p, nk)) return reject(KDA_ERR_ALIAS);
-  if (overlap(o, nv, v, nv) || overlap(o, nv, beta, nb) || overlap(o, nv, state_in, ns) ||
+  if (overlap(o, nv, z, nz) || overlap(o, nv, v, nv) || overlap(o, nv, beta, nb) || overlap(o, nv, state_in, ns) ||
       overlap(o, nv, state_out, ns))
     return reject(KDA_ERR_ALIAS);
   for (const void* p : ins)
     if (overlap(state_out, ns, p, nk)) return reject(KDA_ERR_ALIAS);
-  if (overlap(state_out, ns, v, nv) || overlap(state_out, ns, beta, nb)) return reject(KDA_ERR_ALIAS);
+  if (overlap(state_out, ns, z, nz) || overlap(state_out, ns, v, nv) || overlap(state_out, ns, beta, nb))
+    return reject(KDA_ERR_ALIAS);
   if (state_out && state_in && state_out != state_in && overlap(state_out, ns, state_in, ns))
     return reject(KDA_ERR_ALIAS);
   FwdPlan plan;
@@ -166,32 +174,62 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* z, co
     }
   } else {
     e = launch_fwd(dtype == KDA_BF16, plan, q, k, v, z, A_log, dt_bias, beta, state_in, scale, o, state_out, B, H, T,
-                   K, V, s);
+                   K, V, zc, s);
   }
   if (e != hipSuccess) return reject(KDA_ERR_HIP);
   g_counters[KDA_COUNTER_CHUNK_FWD].fetch_add(1, std::memory_order_relaxed);
   return KDA_OK;
 }
 
-int kda_recurrent_step(const void* q, const void* k, const void* v, const void* z, const float* A_log,
-                       const float* dt_bias, const void* beta, float* state, float scale, void* o, int B, int H,
-                       int K, int V, int dtype, void* stream) {
+// kda_recurrent_step (zc = 1) and kda_recurrent_step_scalar (zc = 0).
+static int recurrent_step_impl(const void* q, const void* k, const void* v, const void* z, const float* A_log,
+                               const float* dt_bias, const void* beta, float* state, float scale, void* o, int B,
+                               int H, int K, int V, int dtype, void* stream, int zc) {
   if (!q || !k || !v || !z || !A_log || !beta || !state || !o) return reject(KDA_ERR_NULL);
   if (dtype != KDA_F32 && dtype != KDA_BF16) return reject(KDA_ERR_DTYPE);
   if (B < 1 || H < 1 || !valid_dim(K) || !valid_dim(V)) return reject(KDA_ERR_SHAPE);
   const size_t es = esize(dtype);
   const size_t nk = (size_t)B * H * K * es, nv = (size_t)B * H * V * es, ns = (size_t)B * H * K * V * 4;
-  if (overlap(o, nv, q, nk) || overlap(o, nv, k, nk) || overlap(o, nv, z, nk) || overlap(o, nv, v, nv) ||
+  const size_t nz = zc ? nk : (size_t)B * H * es;
+  if (overlap(o, nv, q, nk) || overlap(o, nv, k, nk) || overlap(o, nv, z, nz) || overlap(o, nv, v, nv) ||
       overlap(o, nv, beta, (size_t)B * H * es) || overlap(o, nv, state, ns) || overlap(state, ns, q, nk) ||
-      overlap(state, ns, k, nk) || overlap(state, ns, z, nk) || overlap(state, ns, v, nv))
+      overlap(state, ns, k, nk) || overlap(state, ns, z, nz) || overlap(state, ns, v, nv))
     return reject(KDA_ERR_ALIAS);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dtype == KDA_BF16
-                     ? launch_step<bf16_t>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, K, V, s)
-                     : launch_step<float>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, K, V, s);
+                     ? launch_step<bf16_t>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, K, V, zc, s)
+                     : launch_step<float>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, K, V, zc, s);
   if (e != hipSuccess) return reject(KDA_ERR_HIP);
   g_counters[KDA_COUNTER_RECURRENT_STEP].fetch_add(1, std::memory_order_relaxed);
   return KDA_OK;
+}
+
+extern "C" {
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* z, const float* A_log,
+                  const float* dt_bias, const void* beta, const float* state_in, float scale, int chunk, void* o,
+                  float* state_out, int B, int H, int T, int K, int V, int dtype, void* stream) {
+  return chunk_fwd_impl(q, k, v, z, A_log, dt_bias, beta, state_in, scale, chunk, o, state_out, B, H, T, K, V, dtype,
+                        stream, 1);
+}
+
+int kda_chunk_fwd_scalar(const void* q, const void* k, const void* v, const void* a, const float* A_log,
+                         const float* dt_bias, const void* beta, const float* state_in, float scale, int chunk,
+                         void* o, float* state_out, int B, int H, int T, int K, int V, int dtype, void* stream) {
+  return chunk_fwd_impl(q, k, v, a, A_log, dt_bias, beta, state_in, scale, chunk, o, state_out, B, H, T, K, V, dtype,
+                        stream, 0);
+}
+
+int kda_recurrent_step(const void* q, const void* k, const void* v, const void* z, const float* A_log,
+                       const float* dt_bias, const void* beta, float* state, float scale, void* o, int B, int H,
+                       int K, int V, int dtype, void* stream) {
+  return recurrent_step_impl(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, K, V, dtype, stream, 1);
+}
+
+int kda_recurrent_step_scalar(const void* q, const void* k, const void* v, const void* a, const float* A_log,
+                              const float* dt_bias, const void* beta, float* state, float scale, void* o, int B,
+                              int H, int K, int V, int dtype, void* stream) {
+  return recurrent_step_impl(q, k, v, a, A_log, dt_bias, beta, state, scale, o, B, H, K, V, dtype, stream, 0);
 }
 
 size_t kda_chunk_bwd_workspace_bytes(int B, int H, int T, int K, int V, int chunk) {

@@ -332,10 +332,10 @@ hipError_t launch_chunk_bwd(const float* q, const float* k, const float* v, cons
   hipError_t err = hipSuccess;
   if (T > 0) {
     switch (p.fwd.KD) {
-      case 16: err = launch_chunk_fwd_kd<float, 16>(p.fwd.VT, p.fwd.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, nullptr, nullptr, (float*)ws, B, H, T, K, V, s); break;
-      case 32: err = launch_chunk_fwd_kd<float, 32>(p.fwd.VT, p.fwd.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, nullptr, nullptr, (float*)ws, B, H, T, K, V, s); break;
-      case 64: err = launch_chunk_fwd_kd<float, 64>(p.fwd.VT, p.fwd.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, nullptr, nullptr, (float*)ws, B, H, T, K, V, s); break;
-      default: err = launch_chunk_fwd_kd<float, 128>(p.fwd.VT, p.fwd.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, nullptr, nullptr, (float*)ws, B, H, T, K, V, s); break;
+      case 16: err = launch_chunk_fwd_kd<float, 16>(p.fwd.VT, p.fwd.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, nullptr, nullptr, (float*)ws, B, H, T, K, V, 1, s); break;
+      case 32: err = launch_chunk_fwd_kd<float, 32>(p.fwd.VT, p.fwd.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, nullptr, nullptr, (float*)ws, B, H, T, K, V, 1, s); break;
+      case 64: err = launch_chunk_fwd_kd<float, 64>(p.fwd.VT, p.fwd.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, nullptr, nullptr, (float*)ws, B, H, T, K, V, 1, s); break;
+      default: err = launch_chunk_fwd_kd<float, 128>(p.fwd.VT, p.fwd.C, q, k, v, z, A_log, dt_bias, beta, state_in, scale, nullptr, nullptr, (float*)ws, B, H, T, K, V, 1, s); break;
     }
     if (err != hipSuccess) return err;
   }

@@ -24,6 +24,9 @@
 // applied per channel to the row operand.  If some half-block decays by more than
 // 2^thresh in some channel, L or R could overflow: that chunk is then evaluated
 // token by token (exact, slower) instead.
+//
+// Gate layout: zc = 1 takes z (B,H,T,K) and dt_bias (H,K); zc = 0 is the scalar-decay
+// case, z (B,H,T) and dt_bias (H), one gate value per token shared by every channel.
 #pragma once
 
 #include "kda_common.h"
@@ -118,7 +121,7 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
                  const Tin* __restrict__ z, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
                  const Tin* __restrict__ beta, const float* state_in, float scale, Tin* __restrict__ o,
                  float* state_out, float* __restrict__ ckpt, int H, int T, int K, int V, int n_vtiles, int total_wg,
-                 float thresh) {
+                 float thresh, int zc) {
   using Cfg = FwdCfg<Tin, KD, VT, C>;
   using Top = Tin;
   using MM = Mfma<Top>;
@@ -212,7 +215,7 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
         const size_t a = (tb + min(tn + 16 * kb + t, T - 1)) * K + 2 * kc2;
         rk[t] = Pair<Tin>::load(k + a);
         rq[t] = Pair<Tin>::load(q + a);
-        rz[t] = Pair<Tin>::load(z + a);
+        rz[t] = zc ? Pair<Tin>::load(z + a) : Pair<Tin>::dup(z[tb + min(tn + 16 * kb + t, T - 1)]);
       }
     }
     if (has_v) {
@@ -248,8 +251,8 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
     bool bad = false;
     if (has_k) {
       const int c = 2 * kc2, b = kb;
-      const float dtb0 = dt_bias ? dt_bias[h * K + c] : 0.0f;
-      const float dtb1 = dt_bias ? dt_bias[h * K + c + 1] : 0.0f;
+      const float dtb0 = dt_bias ? dt_bias[zc ? h * K + c : h] : 0.0f;
+      const float dtb1 = dt_bias ? dt_bias[zc ? h * K + c + 1 : h] : 0.0f;
       float g0[8], g1[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -323,8 +326,8 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
         const size_t tok = tokbase + i;
         for (int c = tid; c < KD; c += 256) {
           if (c < K) {
-            const float dtb = dt_bias ? dt_bias[h * K + c] : 0.0f;
-            sAl[c] = fast_exp2(-mult2 * softplus_f(to_f<Tin>(z[tok * K + c]) + dtb, true));
+            const float dtb = dt_bias ? dt_bias[zc ? h * K + c : h] : 0.0f;
+            sAl[c] = fast_exp2(-mult2 * softplus_f(to_f<Tin>(z[zc ? tok * K + c : tok]) + dtb, true));
             sKk[c] = to_f<Tin>(k[tok * K + c]);
             sQq[c] = scale * to_f<Tin>(q[tok * K + c]);
           } else {
@@ -610,13 +613,14 @@ chunk_fwd_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin
 template <typename Tin, int KD, int VT, int C>
 hipError_t launch_chunk_fwd_inst(const void* q, const void* k, const void* v, const void* z, const float* A_log,
                                  const float* dt_bias, const void* beta, const float* state_in, float scale, void* o,
-                                 float* state_out, float* ckpt, int B, int H, int T, int K, int V, hipStream_t s) {
+                                 float* state_out, float* ckpt, int B, int H, int T, int K, int V, int zc,
+                                 hipStream_t s) {
   const int nvt = (V + VT - 1) / VT;
   const int total = B * H * nvt;
   const float thresh = sizeof(Tin) == 2 ? 64.0f : 24.0f;
   hipLaunchKernelGGL((chunk_fwd_kernel<Tin, KD, VT, C>), dim3(total), dim3(256), 0, s, (const Tin*)q,
                      (const Tin*)k, (const Tin*)v, (const Tin*)z, A_log, dt_bias, (const Tin*)beta, state_in, scale,
-                     (Tin*)o, state_out, ckpt, H, T, K, V, nvt, total, thresh);
+                     (Tin*)o, state_out, ckpt, H, T, K, V, nvt, total, thresh, zc);
   return hipGetLastError();
 }
 

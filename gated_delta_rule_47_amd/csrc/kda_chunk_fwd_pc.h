@@ -51,6 +51,11 @@
 // diag(Gamma_C) S + KD^T U = diag(D0) (G0 S + KR^T U) since Gamma_C = G0 D0.  Every factor
 // is 2^x with |x| at most one 16-token half of the block's decay; a block where that
 // exceeds 2^thresh in some channel is evaluated token by token by the V waves.
+//
+// SG (scalar decay): z is (B,H,T) and dt_bias (H): one gate value per token and head
+// shares every key channel.  The E waves then load one gate input per token, evaluate the
+// gate and the decay scan once per token and use one pair of factors for both channels of
+// a lane; everything else is the per-channel kernel unchanged.
 #pragma once
 
 #include <type_traits>
@@ -227,7 +232,7 @@ __device__ __forceinline__ void quarter_scan(float a, int g, float& total, float
 // strong for the factorised MFMA path; kept out of line so that the register budget of
 // the walk is not shaped by this rare path.  Pointers are the head's rows; operands come
 // through buffer resources, four key channels per load.
-template <int NMT>
+template <int NMT, bool SG>
 __device__ __attribute__((noinline)) void token_block(float* stl, const bf16_t* q, const bf16_t* k,
                                                      const bf16_t* v, const bf16_t* z, const bf16_t* beta,
                                                      const float* dt_bias, bf16_t* o, int T, int K, int V, int v0,
@@ -235,12 +240,13 @@ __device__ __attribute__((noinline)) void token_block(float* stl, const bf16_t* 
                                                      int lane, int col) {
   constexpr unsigned kOOB = 0xFFFFFFF0u;
   const int g = lane >> 4;
-  const __amdgpu_buffer_rsrc_t tz = make_rsrc(z, (unsigned)(T * K * 2));
+  const __amdgpu_buffer_rsrc_t tz = make_rsrc(z, (unsigned)(T * (SG ? 1 : K) * 2));
   const __amdgpu_buffer_rsrc_t tk = make_rsrc(k, (unsigned)(T * K * 2));
   const __amdgpu_buffer_rsrc_t tq = make_rsrc(q, (unsigned)(T * K * 2));
   const __amdgpu_buffer_rsrc_t tv = make_rsrc(v, (unsigned)(T * V * 2));
   const __amdgpu_buffer_rsrc_t tbe = make_rsrc(beta, (unsigned)(T * 2));
-  const __amdgpu_buffer_rsrc_t tdb = make_rsrc(dt_bias, dt_bias ? K * 4 : 0u);
+  const __amdgpu_buffer_rsrc_t tdb = make_rsrc(dt_bias, dt_bias ? (SG ? 4u : K * 4) : 0u);
+  const float dtbs = (SG && dt_bias) ? dt_bias[0] : 0.0f;   // the head's one bias (SG)
   const __amdgpu_buffer_rsrc_t to = make_rsrc(o, o ? (unsigned)(T * V * 2) : 0u);
   auto elem = [](u32x2 w, int r) __attribute__((always_inline)) {
     const uint32_t u = r < 2 ? w.x : w.y;
@@ -251,19 +257,22 @@ __device__ __attribute__((noinline)) void token_block(float* stl, const bf16_t* 
     const float vv =
         col < vcols ? bf2f(__builtin_amdgcn_raw_buffer_load_b16(tv, (unsigned)((tok * V + v0 + col) * 2), 0, 0)) : 0.0f;
     const float bt = bf2f(__builtin_amdgcn_raw_buffer_load_b16(tbe, (unsigned)(tok * 2), 0, 0));
+    const float zs = SG ? bf2f(__builtin_amdgcn_raw_buffer_load_b16(tz, (unsigned)(tok * 2), 0, 0)) : 0.0f;
     float rp = 0.0f;
     for (int mt = 0; mt < NMT; ++mt) {        // S' = diag(alpha) S, partial S'^T k
       const int c0 = 16 * mt + 4 * g;
       const bool ok = c0 < K;                 // K is a multiple of 4
       const unsigned off = ok ? (unsigned)((tok * K + c0) * 2) : kOOB;
-      const u32x2 zz = __builtin_amdgcn_raw_buffer_load_b64(tz, off, 0, 0);
+      const u32x2 zz = SG ? u32x2{0u, 0u} : __builtin_amdgcn_raw_buffer_load_b64(tz, off, 0, 0);
       const u32x2 kk = __builtin_amdgcn_raw_buffer_load_b64(tk, off, 0, 0);
       const floatx4 db =
-          __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(tdb, ok ? (unsigned)(c0 * 4) : kOOB, 0, 0));
+          SG ? floatx4{dtbs, dtbs, dtbs, dtbs}
+             : __builtin_bit_cast(floatx4,
+                                  __builtin_amdgcn_raw_buffer_load_b128(tdb, ok ? (unsigned)(c0 * 4) : kOOB, 0, 0));
       floatx4 st = *reinterpret_cast<const floatx4*>(stl + mt * 256);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        st[r] *= ok ? fast_exp2(-mult2 * softplus_f(elem(zz, r) + db[r], true)) : 0.0f;
+        st[r] *= ok ? fast_exp2(-mult2 * softplus_f((SG ? zs : elem(zz, r)) + db[r], true)) : 0.0f;
         rp += st[r] * elem(kk, r);
       }
       *reinterpret_cast<floatx4*>(stl + mt * 256) = st;
@@ -292,7 +301,7 @@ __device__ __attribute__((noinline)) void token_block(float* stl, const bf16_t* 
   }
 }
 
-template <int KD, int VT, int C>
+template <int KD, int VT, int C, bool SG>
 __global__ void __launch_bounds__(1024)
 chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                     const bf16_t* __restrict__ z, const float* __restrict__ A_log,
@@ -372,36 +381,44 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     const bool kact = KD == 128 || 2 * pair < K;  // (K = KD = 128: every pair is a channel pair)
     const bool precise = gmul > 64.0f;
     // dt_bias in log2 units: the gate is taken as -gmul softplus2(z log2(e) + dt_bias log2(e))
-    const float dtb0 = (kact && dt_bias) ? dt_bias[h * K + 2 * pair] * kLog2e : 0.0f;
-    const float dtb1 = (kact && dt_bias) ? dt_bias[h * K + 2 * pair + 1] * kLog2e : 0.0f;
+    const float dtb0 = (kact && dt_bias) ? dt_bias[SG ? h : h * K + 2 * pair] * kLog2e : 0.0f;
+    const float dtb1 = (kact && dt_bias) ? dt_bias[SG ? h : h * K + 2 * pair + 1] * kLog2e : 0.0f;
     // per-head buffer resources: offsets past the head's T tokens read as 0
     const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(k + tb * K, (unsigned)(T * K * 2));
     const __amdgpu_buffer_rsrc_t rs_q = make_rsrc(q + tb * K, (unsigned)(T * K * 2));
-    const __amdgpu_buffer_rsrc_t rs_z = make_rsrc(z + tb * K, (unsigned)(T * K * 2));
+    const __amdgpu_buffer_rsrc_t rs_z = SG ? make_rsrc(z + tb, (unsigned)(T * 2)) : make_rsrc(z + tb * K, (unsigned)(T * K * 2));
 
     // k, q, z of this lane's channel pair and four tokens, loaded one block ahead into one
     // of two register sets: the walk alternates between them, so a load never targets
     // registers whose previous contents are still to be read.  These 12 loads are the E
     // waves' only memory operations, so the wait for a set leaves the next one in flight.
+    // (SG: the gate inputs stay 16-bit until they are used one step later, so that nothing
+    // consumes a load in the step that issues it)
+    typedef typename std::conditional<SG, unsigned short, uint32_t>::type ZRaw;
     struct Raw {
-      uint32_t k[4], q[4], z[4];
+      uint32_t k[4], q[4];
+      ZRaw z[4];
     };
     // Byte offset of the lane's first row in block 0.  Lanes without a channel pair or
     // without token rows (the second half when C = 16) start at 2^31, past any head's range
     // (a head's rows, plus a block past its end, stay below 2^31 bytes): they read zeros.
     const int rowb = (KD >= 64 ? KD : K) * 2;  // bytes per token row (K = KD unless KD = 32)
     const unsigned vbase = (kact && 16 * half < C) ? (unsigned)((16 * half + tq) * rowb + 4 * pair) : 0x80000000u;
+    // SG: byte offset of the lane's first gate value (one bf16 per token) in block 0
+    const unsigned zbase = (kact && 16 * half < C) ? (unsigned)((16 * half + tq) * 2) : 0x80000000u;
     const int dpoff = kact ? 8 * pair : 0;     // this lane's channel pair in a per-channel fp32 array
     // element offset of the lane's first token row and channel pair in a [token][channel] tile
     const int rowoff = (16 * half + tq) * LD_TK + perm32(2 * pair);
     auto load_qkz = [&](int b, Raw& r) __attribute__((always_inline)) {
       unsigned off = vbase + (unsigned)(b * C * rowb);
       asm volatile("" : "+v"(off));            // one register; the row steps become immediates
+      unsigned zoff = zbase + (unsigned)(b * C * 2);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         r.k[t] = buf_load_b32(rs_k, off + t * rowb);
         r.q[t] = buf_load_b32(rs_q, off + t * rowb);
-        r.z[t] = buf_load_b32(rs_z, off + t * rowb);
+        if constexpr (SG) r.z[t] = __builtin_amdgcn_raw_buffer_load_b16(rs_z, zoff + t * 2, 0, 0);
+        else r.z[t] = buf_load_b32(rs_z, off + t * rowb);
       }
     };
 
@@ -421,7 +438,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       for (int t = 0; t < 4; ++t) {
         rk[t].u = cur.k[t];
         rq[t].u = cur.q[t];
-        rz[t].u = cur.z[t];
+        if constexpr (SG) rz[t] = Pair<bf16_t>::dup((bf16_t)cur.z[t]);
+        else rz[t].u = cur.z[t];
       }
       // the next block's loads (past the last block they fall outside the head's range
       // and read zeros)
@@ -444,7 +462,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         ax = fmaf(-gmul, softplus2_f(fmaf(rz[t].x(), kLog2e, dtb0), PRECISE), ax);
-        ay = fmaf(-gmul, softplus2_f(fmaf(rz[t].y(), kLog2e, dtb1), PRECISE), ay);
+        if constexpr (SG) ay = ax;             // one gate per token: both channels share it
+        else ay = fmaf(-gmul, softplus2_f(fmaf(rz[t].y(), kLog2e, dtb1), PRECISE), ay);
         px[t] = ax;
         py[t] = ay;
       }
@@ -452,7 +471,12 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       // the sum over the half, and the sum over the quarters before the lane's own.
       float sumx, sumy, exx, exy;
       quarter_scan(ax, g, sumx, exx);
-      quarter_scan(ay, g, sumy, exy);
+      if constexpr (SG) {
+        sumy = sumx;
+        exy = exx;
+      } else {
+        quarter_scan(ay, g, sumy, exy);
+      }
       // exponent of token t relative to the reference: G_t - m = px[t] + off (the first
       // half counts back from the reference, the second forward from it)
       const float offx = half == 0 ? exx - sumx : exx;
@@ -476,7 +500,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const float ex = px[t] + offx, ey = py[t] + offy;
-          const float Lx = fast_exp2(ex), Ly = fast_exp2(ey), Rx = fast_exp2(-ex), Ry = fast_exp2(-ey);
+          const float Lx = fast_exp2(ex), Rx = fast_exp2(-ex);
+          const float Ly = SG ? Lx : fast_exp2(ey), Ry = SG ? Rx : fast_exp2(-ey);
           const float kx = rk[t].x(), ky = rk[t].y(), qx = rq[t].x(), qy = rq[t].y();
           wke[t] = pack_bf16x2(-kx * Lx, -ky * Ly);   // KE is stored negated (V then needs no sign flip of v)
           wqe[t] = pack_bf16x2(qx * Lx, qy * Ly);
@@ -865,9 +890,9 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         float* stl = reinterpret_cast<float*>(sb) + vw * (NMT * 256) + ln * 4;
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) *reinterpret_cast<floatx4*>(stl + mt * 256) = sacc[mt];
-        token_block<NMT>(stl, q + tb * K, k + tb * K, v + tb * V, z + tb * K, beta + tb,
-                         dt_bias ? dt_bias + h * K : nullptr, o ? o + tb * V : nullptr, T, K, V, v0, vcols, t0c, nval,
-                         mult2, scale, ln, 16 * vw + ll);
+        token_block<NMT, SG>(stl, q + tb * K, k + tb * K, v + tb * V, SG ? z + tb : z + tb * K, beta + tb,
+                             dt_bias ? dt_bias + (SG ? h : h * K) : nullptr, o ? o + tb * V : nullptr, T, K, V, v0,
+                             vcols, t0c, nval, mult2, scale, ln, 16 * vw + ll);
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) sacc[mt] = *reinterpret_cast<const floatx4*>(stl + mt * 256);
         wait_vm();                             // the token path's loads
@@ -921,13 +946,13 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   }
 }
 
-template <int KD, int VT, int C>
+template <int KD, int VT, int C, bool SG>
 hipError_t launch_chunk_fwd_pc_inst(const void* q, const void* k, const void* v, const void* z, const float* A_log,
                                     const float* dt_bias, const void* beta, const float* state_in, float scale, void* o,
                                     float* state_out, int B, int H, int T, int K, int V, hipStream_t s) {
   const int nvt = (V + VT - 1) / VT;
   const int total = B * H * nvt;
-  hipLaunchKernelGGL((chunk_fwd_pc_kernel<KD, VT, C>), dim3(total), dim3(PcCfg<KD, VT, C>::NWAVES * 64), 0, s,
+  hipLaunchKernelGGL((chunk_fwd_pc_kernel<KD, VT, C, SG>), dim3(total), dim3(PcCfg<KD, VT, C>::NWAVES * 64), 0, s,
                      (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)z, A_log, dt_bias,
                      (const bf16_t*)beta, state_in, scale, (bf16_t*)o, state_out, H, T, K, V, nvt, total, 96.0f);
   return hipGetLastError();

@@ -135,6 +135,12 @@ template <> struct Pair<bf16_t> {
     r.u = *reinterpret_cast<const uint32_t*>(p);
     return r;
   }
+  // one value for both elements (a scalar-decay gate input serves every channel)
+  static __device__ __forceinline__ Pair dup(bf16_t x) {
+    Pair r;
+    r.u = ((uint32_t)x << 16) | (uint32_t)x;
+    return r;
+  }
   __device__ __forceinline__ float x() const { return __uint_as_float(u << 16); }
   __device__ __forceinline__ float y() const { return __uint_as_float(u & 0xffff0000u); }
 };
@@ -143,6 +149,11 @@ template <> struct Pair<float> {
   static __device__ __forceinline__ Pair load(const float* p) {
     Pair r;
     r.f = *reinterpret_cast<const float2*>(p);
+    return r;
+  }
+  static __device__ __forceinline__ Pair dup(float x) {
+    Pair r;
+    r.f = float2{x, x};
     return r;
   }
   __device__ __forceinline__ float x() const { return f.x; }

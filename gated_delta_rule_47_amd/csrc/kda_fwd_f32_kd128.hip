@@ -8,11 +8,11 @@ template <>
 hipError_t launch_chunk_fwd_kd<float, 128>(int VT, int C, const void* q, const void* k, const void* v, const void* z,
                                       const float* A_log, const float* dt_bias, const void* beta,
                                       const float* state_in, float scale, void* o, float* state_out, float* ckpt,
-                                      int B, int H, int T, int K, int V, hipStream_t s) {
+                                      int B, int H, int T, int K, int V, int zc, hipStream_t s) {
 #define KDA_CASE(VT_, C_)                                                                                  \
   if (VT == VT_ && C == C_)                                                                                \
     return launch_chunk_fwd_inst<float, 128, VT_, C_>(q, k, v, z, A_log, dt_bias, beta, state_in, scale, o,     \
-                                                   state_out, ckpt, B, H, T, K, V, s);
+                                                   state_out, ckpt, B, H, T, K, V, zc, s);
   KDA_CASE(16, 16)
   KDA_CASE(16, 32)
   KDA_CASE(32, 16)

@@ -127,7 +127,7 @@ __global__ void __launch_bounds__(256) step_kernel(const Tin* __restrict__ q, co
                                                    const Tin* __restrict__ v, const Tin* __restrict__ z,
                                                    const float* __restrict__ A_log, const float* __restrict__ dt_bias,
                                                    const Tin* __restrict__ beta, float* __restrict__ state,
-                                                   float scale, Tin* __restrict__ o, int H, int V) {
+                                                   float scale, Tin* __restrict__ o, int H, int V, int zc) {
   constexpr int NRG = cmin(256 / VTS, K);   // row groups
   constexpr int RPT = K / NRG;              // rows per thread
   __shared__ float sAl[K], sK[K], sQ[K], sRed[NRG * VTS];
@@ -142,7 +142,8 @@ __global__ void __launch_bounds__(256) step_kernel(const Tin* __restrict__ q, co
 
   const float mult = gate_multiplier(A_log[h]);
   for (int c = tid; c < K; c += NRG * VTS) {
-    const float x = to_f<Tin>(z[(size_t)bh * K + c]) + (dt_bias ? dt_bias[h * K + c] : 0.0f);
+    // zc = 0: the scalar-decay layout, one gate input per (b, h) and one bias per head
+    const float x = to_f<Tin>(z[zc ? (size_t)bh * K + c : (size_t)bh]) + (dt_bias ? dt_bias[zc ? h * K + c : h] : 0.0f);
     sAl[c] = fast_exp2(-mult * softplus_f(x, true) * kLog2e);
     sK[c] = to_f<Tin>(k[(size_t)bh * K + c]);
     sQ[c] = scale * to_f<Tin>(q[(size_t)bh * K + c]);
@@ -229,36 +230,36 @@ template hipError_t launch_gate_bwd<bf16_t>(const void*, const float*, const flo
 template <typename Tin, int K, int VTS>
 static hipError_t launch_step_kv(const void* q, const void* k, const void* v, const void* z, const float* A_log,
                                  const float* dt_bias, const void* beta, float* state, float scale, void* o, int B,
-                                 int H, int V, hipStream_t s) {
+                                 int H, int V, int zc, hipStream_t s) {
   constexpr int NRG = cmin(256 / VTS, K);
   const int grid = B * H * (V / VTS);
   hipLaunchKernelGGL((step_kernel<Tin, K, VTS>), dim3(grid), dim3(NRG * VTS), 0, s, (const Tin*)q, (const Tin*)k,
-                     (const Tin*)v, (const Tin*)z, A_log, dt_bias, (const Tin*)beta, state, scale, (Tin*)o, H, V);
+                     (const Tin*)v, (const Tin*)z, A_log, dt_bias, (const Tin*)beta, state, scale, (Tin*)o, H, V, zc);
   return hipGetLastError();
 }
 
 template <typename Tin, int K>
 static hipError_t launch_step_k(const void* q, const void* k, const void* v, const void* z, const float* A_log,
                                 const float* dt_bias, const void* beta, float* state, float scale, void* o, int B,
-                                int H, int V, hipStream_t s) {
+                                int H, int V, int zc, hipStream_t s) {
   switch (V) {
-    case 8: return launch_step_kv<Tin, K, 8>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, s);
-    case 16: return launch_step_kv<Tin, K, 16>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, s);
-    case 32: return launch_step_kv<Tin, K, 32>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, s);
-    default: return launch_step_kv<Tin, K, 64>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, s);
+    case 8: return launch_step_kv<Tin, K, 8>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, zc, s);
+    case 16: return launch_step_kv<Tin, K, 16>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, zc, s);
+    case 32: return launch_step_kv<Tin, K, 32>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, zc, s);
+    default: return launch_step_kv<Tin, K, 64>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, zc, s);
   }
 }
 
 template <typename Tin>
 hipError_t launch_step(const void* q, const void* k, const void* v, const void* z, const float* A_log,
                        const float* dt_bias, const void* beta, float* state, float scale, void* o, int B, int H,
-                       int K, int V, hipStream_t s) {
+                       int K, int V, int zc, hipStream_t s) {
   switch (K) {
-    case 8: return launch_step_k<Tin, 8>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, s);
-    case 16: return launch_step_k<Tin, 16>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, s);
-    case 32: return launch_step_k<Tin, 32>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, s);
-    case 64: return launch_step_k<Tin, 64>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, s);
-    default: return launch_step_k<Tin, 128>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, s);
+    case 8: return launch_step_k<Tin, 8>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, zc, s);
+    case 16: return launch_step_k<Tin, 16>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, zc, s);
+    case 32: return launch_step_k<Tin, 32>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, zc, s);
+    case 64: return launch_step_k<Tin, 64>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, zc, s);
+    default: return launch_step_k<Tin, 128>(q, k, v, z, A_log, dt_bias, beta, state, scale, o, B, H, V, zc, s);
   }
 }
 
@@ -267,9 +268,9 @@ template hipError_t launch_gate<float>(const void*, const float*, const float*, 
 template hipError_t launch_gate<bf16_t>(const void*, const float*, const float*, float*, float*, int, int, int, int,
                                         hipStream_t);
 template hipError_t launch_step<float>(const void*, const void*, const void*, const void*, const float*, const float*,
-                                       const void*, float*, float, void*, int, int, int, int, hipStream_t);
+                                       const void*, float*, float, void*, int, int, int, int, int, hipStream_t);
 template hipError_t launch_step<bf16_t>(const void*, const void*, const void*, const void*, const float*,
-                                        const float*, const void*, float*, float, void*, int, int, int, int,
+                                        const float*, const void*, float*, float, void*, int, int, int, int, int,
                                         hipStream_t);
 
 }  // namespace kda

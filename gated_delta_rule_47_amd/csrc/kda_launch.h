@@ -22,7 +22,10 @@ hipError_t launch_gate_bwd(const void* z, const float* A_log, const float* dt_bi
 template <typename Tin>
 hipError_t launch_step(const void* q, const void* k, const void* v, const void* z, const float* A_log,
                        const float* dt_bias, const void* beta, float* state, float scale, void* o, int B, int H,
-                       int K, int V, hipStream_t s);
+                       int K, int V, int zc, hipStream_t s);
+
+// Gate layout of the forward and step launchers: zc = 1, z is (B,H,T,K) and dt_bias (H,K);
+// zc = 0, the scalar-decay case, z is (B,H,T) and dt_bias (H).
 
 // Chunked forward: instance chosen by (padded key dim KD, value tile VT, chunk C).
 // ckpt (nullable) receives the state at every chunk start: (B,H,ceil(T/C),K,V) fp32.
@@ -30,13 +33,13 @@ template <typename Tin, int KD>
 hipError_t launch_chunk_fwd_kd(int VT, int C, const void* q, const void* k, const void* v, const void* z,
                                const float* A_log, const float* dt_bias, const void* beta, const float* state_in,
                                float scale, void* o, float* state_out, float* ckpt, int B, int H, int T, int K, int V,
-                               hipStream_t s);
+                               int zc, hipStream_t s);
 
-// Pipelined bf16 forward (8 waves, internal blocks of C <= 32 tokens).
+// Pipelined bf16 forward (16 waves, internal blocks of C <= 32 tokens).
 template <int KD>
 hipError_t launch_chunk_fwd_pc_kd(int VT, int C, const void* q, const void* k, const void* v, const void* z,
                                   const float* A_log, const float* dt_bias, const void* beta, const float* state_in,
-                                  float scale, void* o, float* state_out, int B, int H, int T, int K, int V,
+                                  float scale, void* o, float* state_out, int B, int H, int T, int K, int V, int zc,
                                   hipStream_t s);
 
 // Forward tiling actually used for (dtype, K, V, chunk): padded key dim, value tile

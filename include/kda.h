@@ -111,6 +111,29 @@ int kda_recurrent_step(const void* q, const void* k, const void* v, const void* 
                        float* state, float scale, void* o,
                        int B, int H, int K, int V, int dtype, void* stream);
 
+/* Scalar-decay special case of kda_chunk_fwd: one gate input per token and head and
+ * one bias per head, so every key channel of a head decays by the same factor,
+ *   g[b,h,t] = -exp(clamp(A_log[h], -10, 20)) * softplus(a[b,h,t] + dt_bias[h])
+ * (the released gate of the "kdafix" page, "Fix 1 -- decay form", with an input that
+ * is constant over the channels).  The result equals kda_chunk_fwd with z[b,h,t,:] =
+ * a[b,h,t] and dt_bias[h,:] = dt_bias[h].
+ *   a        (B,H,T) `dtype`, aligned to one element
+ *   dt_bias  (H) f32 or NULL (= 0)
+ * Every other argument, layout, alignment rule, error and the aliasing rules are those
+ * of kda_chunk_fwd (a must not alias o or state_out). */
+int kda_chunk_fwd_scalar(const void* q, const void* k, const void* v, const void* a,
+                         const float* A_log, const float* dt_bias, const void* beta,
+                         const float* state_in, float scale, int chunk,
+                         void* o, float* state_out,
+                         int B, int H, int T, int K, int V, int dtype, void* stream);
+
+/* Decode step under the scalar decay: as kda_recurrent_step with a (B,H) `dtype` (one
+ * gate input per sequence and head) and dt_bias (H) f32 or NULL. */
+int kda_recurrent_step_scalar(const void* q, const void* k, const void* v, const void* a,
+                              const float* A_log, const float* dt_bias, const void* beta,
+                              float* state, float scale, void* o,
+                              int B, int H, int K, int V, int dtype, void* stream);
+
 /* Bytes of device workspace kda_chunk_bwd needs for these sizes (0 on bad sizes). */
 size_t kda_chunk_bwd_workspace_bytes(int B, int H, int T, int K, int V, int chunk);
 

@@ -1,7 +1,8 @@
 """The C ABI: the library loads, exports every entry point include/kda.h declares,
 and its host-only functions behave as documented.  No GPU work is launched here:
-the argument-error cases fail validation before any HIP call (and are skipped on
-a machine with a GPU, where tests/test_gpu_abi.py covers them with real buffers).
+the argument-error cases fail validation before any HIP call.  They pass fake
+device addresses, so they are skipped wherever a GPU is visible: a validation
+mistake must never turn into a launch on fake pointers.
 """
 import ctypes
 import os
@@ -74,7 +75,7 @@ def _gpu_visible():
         return False
 
 
-@pytest.mark.skipif(_gpu_visible(), reason="covered with real device buffers by the GPU ABI tests")
+@pytest.mark.skipif(_gpu_visible(), reason="fake device pointers: CPU-only check")
 def test_argument_errors_before_launch():
     lib = _lib()
     P = ctypes.c_void_p
@@ -131,3 +132,30 @@ def test_argument_errors_before_launch():
     rej1 = (ctypes.c_ulonglong * 6)()
     lib.kda_get_counters(rej1, 6)
     assert rej1[4] - rej0[4] == 28 and list(rej1[:4]) == list(rej0[:4]) and rej1[5] == rej0[5]
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake device pointers: CPU-only check")
+def test_scalar_decay_argument_errors_before_launch():
+    lib = _lib()
+    P = ctypes.c_void_p
+    q, k, v, a, A, dt, b, s_in, o, s_out = [P(0x10000 * (i + 1)) for i in range(10)]
+    rej0 = (ctypes.c_ulonglong * 6)()
+    lib.kda_get_counters(rej0, 6)
+    f = lib.kda_chunk_fwd_scalar
+    assert f(q, k, v, None, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 8, 1, None) == -1
+    assert f(q, k, v, a, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 8, 9, None) == -3
+    assert f(q, k, v, a, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 24, 1, None) == -2
+    assert f(q, k, v, a, A, dt, b, s_in, 0.1, 8, o, s_out, 1, 1, 16, 8, 8, 1, None) == -4
+    # the gate input needs one-element alignment only; q, k, v keep the two-element rule
+    assert f(q, k, v, P(0x40001), A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 8, 1, None) == -8
+    assert f(q, P(0x20002), v, a, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 8, 1, None) == -8
+    # o or state_out over the gate input (B*H*T elements)
+    assert f(q, k, v, a, A, dt, b, s_in, 0.1, 64, P(a.value + 2), s_out, 1, 1, 16, 8, 8, 1, None) == -5
+    assert f(q, k, v, a, A, dt, b, s_in, 0.1, 64, o, P(a.value - 4), 1, 1, 16, 8, 8, 0, None) == -5
+    g = lib.kda_recurrent_step_scalar
+    assert g(q, k, v, None, A, dt, b, s_in, 0.1, o, 1, 1, 8, 8, 0, None) == -1
+    assert g(q, k, v, a, A, dt, b, s_in, 0.1, o, 1, 1, 8, 12, 0, None) == -2
+    assert g(q, k, v, a, A, dt, b, s_in, 0.1, a, 1, 1, 8, 8, 0, None) == -5
+    rej1 = (ctypes.c_ulonglong * 6)()
+    lib.kda_get_counters(rej1, 6)
+    assert rej1[4] - rej0[4] == 11 and list(rej1[:4]) == list(rej0[:4])

@@ -422,9 +422,12 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       }
     };
 
-    // e1 handles block b, whose buffers sit in slot sl = b % 3 (slp = (b - 1) % 3)
-    auto e1 = [&](auto precise_tag, int b, int sl, int slp, const Raw& cur, Raw& nxt) __attribute__((always_inline)) {
+    // e1 handles block b, whose buffers sit in slot sl = b % 3 (slp = (b - 1) % 3), for the
+    // wave's half HALF (= half, as a constant: each half has its own code)
+    auto e1 = [&](auto precise_tag, auto half_tag, int b, int sl, int slp, const Raw& cur,
+                  Raw& nxt) __attribute__((always_inline)) {
       constexpr bool PRECISE = decltype(precise_tag)::value;
+      constexpr int HALF = decltype(half_tag)::value;
       const int tn = b * C;
       const int nval = min(C, T - tn);
       char* sb = set_at(sl);
@@ -445,14 +448,15 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       // and read zeros)
       load_qkz(b + 1, nxt);
       sched_fence();
-      // D0 of the previous block, for its F (first half; written a step ago).  Read first
-      // and used before this step's first LDS write, so that the wait for it is for it
-      // alone; its registers stay reserved to the end of the step (see below).
-      const float2 dprev = *reinterpret_cast<const float2*>(set_at(slp) + Cfg::SET_D0 + dpoff);
+      // D0 of the previous block, for its F (first half only; written a step ago).  Read
+      // first and used before this step's first LDS write, so that the wait for it is for
+      // it alone.
+      float2 dprev = float2{0.0f, 0.0f};
+      if constexpr (HALF == 0) dprev = *reinterpret_cast<const float2*>(set_at(slp) + Cfg::SET_D0 + dpoff);
       // Tokens at or past nval (a partial last block, or rows 16..31 when C = 16) are
       // identity tokens: their k and q read as 0, and z = -inf makes their gate 0.
-      if (nval < 16 * half + 16) {
-        const int lim = nval - (16 * half + tq);
+      if (nval < 16 * HALF + 16) {
+        const int lim = nval - (16 * HALF + tq);
 #pragma unroll
         for (int t = 0; t < 4; ++t) rz[t].u = t < lim ? rz[t].u : 0xFF80FF80u;
       }
@@ -479,18 +483,18 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       }
       // exponent of token t relative to the reference: G_t - m = px[t] + off (the first
       // half counts back from the reference, the second forward from it)
-      const float offx = half == 0 ? exx - sumx : exx;
-      const float offy = half == 0 ? exy - sumy : exy;
+      const float offx = HALF == 0 ? exx - sumx : exx;
+      const float offy = HALF == 0 ? exy - sumy : exy;
       // first half: G0 = 2^m, and F = D0 G0 of the previous block
       float2 g0 = float2{0.0f, 0.0f}, fp = float2{0.0f, 0.0f};
-      if (half == 0) {
+      if constexpr (HALF == 0) {
         g0 = float2{fast_exp2(sumx), fast_exp2(sumy)};
         fp = float2{dprev.x * g0.x, dprev.y * g0.y};
       }
       const unsigned long long bal = __ballot(kact && fminf(sumx, sumy) < -thresh);
       if (lane == 0) sFlag[sl * Cfg::NE + wave] = bal != 0ull;
       const int c = 2 * pair;
-      if (half == 0 && kact && g == 0) {
+      if (HALF == 0 && kact && g == 0) {
         *reinterpret_cast<float2*>(sG0 + c) = g0;
         if (b > 0) *reinterpret_cast<float2*>(set_at(slp) + Cfg::SET_F + 4 * c) = fp;
       }
@@ -523,12 +527,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         lds_write2_b32<0, R2>(sKR + rowoff, wkr[0], wkr[2]);
         lds_write2_b32<R1, R3>(sKR + rowoff, wkr[1], wkr[3]);
         // D0 = 2^(G_last - m): the second half's last token, whose L it is
-        if (half == 1 && g == 3) *reinterpret_cast<float2*>(sD0 + c) = float2{lx3, ly3};
+        if (HALF == 1 && g == 3) *reinterpret_cast<float2*>(sD0 + c) = float2{lx3, ly3};
       }
-      // (the second half never uses the D0 it read: without this, its registers could be
-      // reused while the read is in flight, and the write would first wait for every LDS
-      // operation of the step; the barrier waits for them anyway)
-      asm volatile("" ::"v"(dprev.x), "v"(dprev.y));
       lds_wait_asm();                          // the asm writes above, before the barrier
     };
 
@@ -537,8 +537,15 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     auto estep = [&](int s, int sl, int slp, const Raw& cur, Raw& nxt) __attribute__((always_inline)) {
       const int b = s + 2;
       if (b < nck) {
-        if (precise) e1(std::true_type{}, b, sl, slp, cur, nxt);
-        else e1(std::false_type{}, b, sl, slp, cur, nxt);
+        using H0 = std::integral_constant<int, 0>;
+        using H1 = std::integral_constant<int, 1>;
+        if (precise) {
+          if (half) e1(std::true_type{}, H1{}, b, sl, slp, cur, nxt);
+          else e1(std::true_type{}, H0{}, b, sl, slp, cur, nxt);
+        } else {
+          if (half) e1(std::false_type{}, H1{}, b, sl, slp, cur, nxt);
+          else e1(std::false_type{}, H0{}, b, sl, slp, cur, nxt);
+        }
       }
       lds_barrier();
     };

@@ -7,7 +7,7 @@
 //                    operands KE, QE, KR (V reads KR^T from KR with transposing LDS
 //                    reads); wave e covers one 16-token half of
 //                    the block and 32 key channels, from q, k, z loaded straight into
-//                    registers one block ahead;
+//                    registers two blocks ahead;
 //   V (waves 8-11):  the state-dependent part, each wave owning 16 value columns and all
 //                    K rows of the fp32 state in accumulator registers: with
 //                    S~ = diag(G0) S,  Y = V - KE S~,  U = (I + A)^-1 diag(beta) Y,
@@ -388,10 +388,12 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     const __amdgpu_buffer_rsrc_t rs_q = make_rsrc(q + tb * K, (unsigned)(T * K * 2));
     const __amdgpu_buffer_rsrc_t rs_z = SG ? make_rsrc(z + tb, (unsigned)(T * 2)) : make_rsrc(z + tb * K, (unsigned)(T * K * 2));
 
-    // k, q, z of this lane's channel pair and four tokens, loaded one block ahead into one
-    // of two register sets: the walk alternates between them, so a load never targets
-    // registers whose previous contents are still to be read.  These 12 loads are the E
-    // waves' only memory operations, so the wait for a set leaves the next one in flight.
+    // k, q, z of this lane's channel pair and four tokens, loaded two blocks ahead into one
+    // of three register sets: block b lives in set b % 3, so a load never targets registers
+    // whose previous contents are still to be read, and each load has two steps to arrive
+    // (one step is about an HBM round trip under this kernel's load; measured, a step-ahead
+    // prefetch left the E waves waiting).  These 12 loads per block are the E waves' only
+    // memory operations, so the wait for a set leaves the two younger ones in flight.
     // (SG: the gate inputs stay 16-bit until they are used one step later, so that nothing
     // consumes a load in the step that issues it)
     typedef typename std::conditional<SG, unsigned short, uint32_t>::type ZRaw;
@@ -401,7 +403,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     };
     // Byte offset of the lane's first row in block 0.  Lanes without a channel pair or
     // without token rows (the second half when C = 16) start at 2^31, past any head's range
-    // (a head's rows, plus a block past its end, stay below 2^31 bytes): they read zeros.
+    // (a head's rows, plus the two blocks past its end that the prefetch reaches, stay below
+    // 2^31 bytes: the boundary checks T + 64 tokens): they read zeros.
     const int rowb = (KD >= 64 ? KD : K) * 2;  // bytes per token row (K = KD unless KD = 32)
     const unsigned vbase = (kact && 16 * half < C) ? (unsigned)((16 * half + tq) * rowb + 4 * pair) : 0x80000000u;
     // SG: byte offset of the lane's first gate value (one bf16 per token) in block 0
@@ -444,10 +447,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         if constexpr (SG) rz[t] = Pair<bf16_t>::dup((bf16_t)cur.z[t]);
         else rz[t].u = cur.z[t];
       }
-      // the next block's loads (past the last block they fall outside the head's range
-      // and read zeros)
-      load_qkz(b + 1, nxt);
-      sched_fence();
+      (void)nxt;                               // (loaded by the step: see estep)
       // D0 of the previous block, for its F (first half only; written a step ago).  Read
       // first and used before this step's first LDS write, so that the wait for it is for
       // it alone.
@@ -532,10 +532,16 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       lds_wait_asm();                          // the asm writes above, before the barrier
     };
 
-    Raw ra, rb;
-    if (nck > 0) load_qkz(0, ra);
+    Raw ra, rb, rc;
+    load_qkz(0, ra);                           // (blocks past the end read zeros)
+    load_qkz(1, rb);
     auto estep = [&](int s, int sl, int slp, const Raw& cur, Raw& nxt) __attribute__((always_inline)) {
       const int b = s + 2;
+      // The loads of the block after next, issued by every step alike (the index is clamped;
+      // blocks past the end read zeros), so that the compiler sees the same load count on
+      // every path and waits for the oldest set only.
+      load_qkz(min(b + 2, nck + 1), nxt);
+      sched_fence();
       if (b < nck) {
         using H0 = std::integral_constant<int, 0>;
         using H1 = std::integral_constant<int, 1>;
@@ -549,15 +555,18 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       }
       lds_barrier();
     };
-    int sl = 0, slp = 2;                       // slots of blocks s + 2 and s + 1
-    for (int s = -2; s < nck; s += 2) {        // two steps per iteration: block s+2 from ra, s+3 from rb
-      estep(s, sl, slp, ra, rb);
-      slp = sl;
-      sl = __builtin_amdgcn_readfirstlane(sl == 2 ? 0 : sl + 1);
-      if (s + 1 < nck) estep(s + 1, sl, slp, rb, ra);
-      slp = sl;
-      sl = __builtin_amdgcn_readfirstlane(sl == 2 ? 0 : sl + 1);
+    // three steps per iteration, so that register sets and LDS slots are fixed per position:
+    // step s handles block s + 2 (set and slot (s + 2) % 3) and loads block s + 4.  The loop
+    // runs whole iterations only (no conditional step inside it), the last one or two steps
+    // follow it: nck + 2 steps in all, as for the other stages.
+    int s = -2;
+    for (; s + 2 < nck; s += 3) {
+      estep(s, 0, 2, ra, rc);
+      estep(s + 1, 1, 0, rb, ra);
+      estep(s + 2, 2, 1, rc, rb);
     }
+    if (s < nck) estep(s, 0, 2, ra, rc);
+    if (s + 1 < nck) estep(s + 1, 1, 0, rb, ra);
   } else if (wave >= Cfg::NE + Cfg::NV) {
     // ================================================================ W waves
     __builtin_amdgcn_s_setprio(2);             // issue ahead of the E waves (see the V waves)

@@ -46,6 +46,18 @@ KERNEL_SOURCES = ("kda_chunk_fwd_pc.h", "kda_common.h")
 KERNEL_NAME = "kda::chunk_fwd_pc_kernel<128,64,32,false>"
 
 
+def kernel_label(wl, scalar_gate=False) -> str:
+    """The forward instance a kda_chunk_fwd call of this workload launches (the tiling rules
+    of the library's forward plan)."""
+    C = min(wl.chunk, 32)
+    if wl.dtype == "bf16":
+        return "kda::chunk_fwd_pc_kernel<%d,%d,%d,%s>" % (max(32, wl.K), min(64, max(16, wl.V)), C,
+                                                         str(scalar_gate).lower())
+    KD = max(16, wl.K)
+    VT = min(16 if KD >= 64 else 64, max(16, wl.V))
+    return "kda::chunk_fwd_kernel<float,%d,%d,%d>" % (KD, VT, wl.chunk if KD < 128 else C)
+
+
 def kernel_source_hash() -> str:
     """sha256 over the sources of the fused bf16 forward kernel: counter-measured traffic
     is only reported while the kernel it was measured on is unchanged."""
@@ -339,7 +351,7 @@ def main():
             traffic = None
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": KERNEL_NAME.replace("32,false>", "%d,%s>" % (min(wl.chunk, 32), str(args.scalar_gate).lower())),
+            "kernel": kernel_label(wl, args.scalar_gate),
             "algorithmic_bytes_per_launch": nbytes,
             "avg_kernel_ms": round(avg_kernel_ms, 4), "min_kernel_ms": round(float(np.min(kern_ms)), 4)}
     cpu = None
@@ -348,7 +360,9 @@ def main():
         print("bench: CPU oracle baseline on %d heads" % workers, file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, n_heads=workers, workers=workers, scalar_gate=args.scalar_gate)
     out = {
-        "metric": METRIC_SCALAR if args.scalar_gate else METRIC, "value": round(tokens / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": ((METRIC_SCALAR if args.scalar_gate else METRIC) if wl.name == "long"
+                   else "KDA chunked-forward tokens/s (B·H·T/s), %s workload%s"
+                   % (wl.name, ", scalar-decay gate" if args.scalar_gate else "")), "value": round(tokens / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "K": wl.K, "V": wl.V, "chunk": wl.chunk,

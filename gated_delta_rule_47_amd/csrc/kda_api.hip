@@ -252,6 +252,7 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z, co
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)z) & 7) return reject(KDA_ERR_ALIGN);
   const size_t need = bwd_workspace_bytes(B, H, T, K, V, chunk);
   if (!workspace || workspace_bytes < need) return reject(KDA_ERR_WORKSPACE);
+  if ((uintptr_t)workspace & 15) return reject(KDA_ERR_ALIGN);
   const size_t nk = (size_t)B * H * T * K * 4, nv = (size_t)B * H * T * V * 4, nb = (size_t)B * H * T * 4;
   const size_t ns = (size_t)B * H * K * V * 4;
   struct Buf { const void* p; size_t n; };

@@ -141,22 +141,31 @@ bwd_reverse_kernel(const float* __restrict__ q, const float* __restrict__ k, con
       }
     }
 
-    // reverse over the chunk's tokens
+    // reverse over the chunk's tokens.  S_{t-1} comes from the checkpoint (t = 0) or from the
+    // recomputed states in scratch; the state a token needs is loaded one token ahead, so
+    // that the load's latency is not on the token chain.
+    auto load_prev = [&](int t, floatx4 (&dst)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!act) {
+          dst[i] = zero4();
+        } else if (t == 0) {
+          dst[i] = *reinterpret_cast<const floatx4*>(ck + (size_t)(4 * a + i) * V + v0 + 4 * b);
+        } else {
+          dst[i] = *reinterpret_cast<const floatx4*>(scr + ((size_t)(t - 1) * K + 4 * a + i) * VT + 4 * b);
+        }
+      }
+    };
+    floatx4 Snext[4];
+    load_prev(n - 1, Snext);
     for (int t = n - 1; t >= 0; --t) {
       const size_t tok = (size_t)bh * T + tc0 + t;
       float Sprev[4][4];                           // S_{t-1}, undecayed
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (t == 0) {
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) Sprev[i][j] = act ? ck[(size_t)(4 * a + i) * V + v0 + 4 * b + j] : 0.0f;
-        } else {
-          floatx4 x = act ? *reinterpret_cast<const floatx4*>(scr + ((size_t)(t - 1) * K + 4 * a + i) * VT + 4 * b)
-                          : zero4();
-#pragma unroll
-          for (int j = 0; j < 4; ++j) Sprev[i][j] = x[j];
-        }
-      }
+        for (int j = 0; j < 4; ++j) Sprev[i][j] = Snext[i][j];
+      if (t > 0) load_prev(t - 1, Snext);
       float al[4], kk[4], qh[4], vv[4], dov[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {

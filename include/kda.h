@@ -54,7 +54,7 @@ typedef enum {
   KDA_ERR_ALIAS = -5,      /* an output buffer aliases an input it must not alias */
   KDA_ERR_HIP = -6,        /* a HIP launch or runtime call failed */
   KDA_ERR_WORKSPACE = -7,  /* workspace NULL or smaller than kda_chunk_bwd_workspace_bytes() */
-  KDA_ERR_ALIGN = -8       /* an activation pointer is not aligned to two elements */
+  KDA_ERR_ALIGN = -8       /* an activation pointer (or kda_chunk_bwd's workspace) is misaligned */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -146,7 +146,8 @@ size_t kda_chunk_bwd_workspace_bytes(int B, int H, int T, int K, int V, int chun
  * Outputs, all float32, none may alias an input:
  *   dq, dk (B,H,T,K) w.r.t. the unscaled q and k;  dv (B,H,T,V);
  *   dg (B,H,T,K) w.r.t. the log-decay g;  dbeta (B,H,T);  dstate_in (B,H,K,V).
- * workspace: device buffer of at least kda_chunk_bwd_workspace_bytes(); its
+ * workspace: device buffer of at least kda_chunk_bwd_workspace_bytes(), 16-byte
+ * aligned (KDA_ERR_ALIGN otherwise: the kernels read it in 16-byte vectors); its
  * contents on entry are ignored.  Currently dtype must be KDA_F32. */
 int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z,
                   const float* A_log, const float* dt_bias, const void* beta,

@@ -117,6 +117,7 @@ def test_argument_errors_before_launch():
     assert lib.kda_chunk_bwd(*args, g[0], 1 << 40, 1, 1, 16, 8, 8, 1, None) == -3
     assert lib.kda_chunk_bwd(*args, None, 0, 1, 1, 16, 8, 8, 0, None) == -7
     assert lib.kda_chunk_bwd(*args, g[0], 16, 1, 1, 16, 8, 8, 0, None) == -7
+    assert lib.kda_chunk_bwd(*args, P(g[0].value + 4), 1 << 40, 1, 1, 16, 8, 8, 0, None) == -8
     # gate adjoint: no output / null input, bad dtype, bad shape, workspace, aliasing
     ws = fake[11]
     assert lib.kda_gate_bwd(z, A, dt, g[0], None, None, None, ws, 1 << 20, 1, 1, 16, 8, 0, None) == -1
@@ -131,7 +132,7 @@ def test_argument_errors_before_launch():
                             None) == -5
     rej1 = (ctypes.c_ulonglong * 6)()
     lib.kda_get_counters(rej1, 6)
-    assert rej1[4] - rej0[4] == 28 and list(rej1[:4]) == list(rej0[:4]) and rej1[5] == rej0[5]
+    assert rej1[4] - rej0[4] == 29 and list(rej1[:4]) == list(rej0[:4]) and rej1[5] == rej0[5]
 
 
 @pytest.mark.skipif(_gpu_visible(), reason="fake device pointers: CPU-only check")

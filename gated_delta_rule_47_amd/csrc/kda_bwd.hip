@@ -28,8 +28,36 @@ namespace kda {
 
 constexpr int kBwdVTMax = 32;
 
+// Sum of x over the lanes l ^ m, m = lo, 2 lo, ..., hi / 2 (so every lane of each group
+// holds the group's total), without the LDS crossbar: the exchanges are DPP lane moves
+// within a row (xor 1 and 2 by quad permutes, xor 8 by rotating the 16-lane row by 8,
+// xor 4 by mirroring the 8-lane halves once the quads already hold equal sums) and the
+// permlane swaps across rows (xor 16 and 32).  The pairs are exactly those of a
+// butterfly, so the sum is the same as with lane shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp_partner(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float xor_sum(float x, int lo, int hi) {
-  for (int m = lo; m < hi; m <<= 1) x += __shfl_xor(x, m);
+  for (int m = lo; m < hi; m <<= 1) {
+    if (m == 1) {
+      x += dpp_partner<0xB1>(x);               // quad_perm [1,0,3,2]
+    } else if (m == 2) {
+      x += dpp_partner<0x4E>(x);               // quad_perm [2,3,0,1]
+    } else if (m == 4 && lo == 1) {
+      x += dpp_partner<0x141>(x);              // row_half_mirror: the quads hold equal sums
+    } else if (m == 8) {
+      x += dpp_partner<0x128>(x);              // row_ror:8 = lane ^ 8 within a row
+    } else if (m == 16) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+      x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else if (m == 32) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+      x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+      x += __shfl_xor(x, m);
+    }
+  }
   return x;
 }
 

@@ -18,9 +18,9 @@
 //      dbeta = k . (dS e).  Nothing uses atomics, so results are deterministic.
 //
 // Thread layout of step 2: thread (a, b) holds rows 4a..4a+3 and value columns
-// 4b..4b+3 of the K x VT tile.  Sums over columns are shuffles across the CB lanes
-// of a row block; sums over rows are shuffles inside the wave plus one LDS exchange
-// between the four waves per token.
+// 4b..4b+3 of the K x VT tile.  Sums over columns are lane exchanges (DPP moves) across
+// the CB lanes of a row block; sums over rows are lane exchanges inside the wave (DPP
+// moves and permlane swaps) plus one LDS exchange between the four waves per token.
 #include "kda_common.h"
 #include "kda_launch.h"
 

@@ -124,3 +124,23 @@ def test_scalar_long_workload_sampled_heads():
     o_ref, S_ref = R.recurrent_scalar(sub["q"], sub["k"], sub["v"], g, sub["beta"], sub["state_in"])
     _check("o", np.stack([host(o[b, h]) for b, h in heads])[None], o_ref, TOL["bf16"])
     _check("state", np.stack([host(S[b, h]) for b, h in heads])[None], S_ref, TOL["bf16"])
+
+
+def test_scalar_T0_state_none_and_in_place():
+    """T = 0 copies state_in to state_out; no initial state equals a zero one; state_out may
+    be state_in (bf16, the pipelined kernel)."""
+    wl = ks.WORKLOADS["nano"].with_(B=1, H=3, K=128, V=128, state="normal:0.1")
+    x = ks.generate(wl, T=90)
+    d = _scalar_inputs(wl, x)
+    e = lambda t: t[:, :, :0]
+    o0, S0 = kda.chunk_fwd_scalar(e(d["q"]), e(d["k"]), e(d["v"]), e(d["a"]), d["A_log"], d["dtb"], e(d["beta"]),
+                                  d["state_in"], chunk=64)
+    assert o0.numel() == 0 and torch.equal(S0, d["state_in"])
+    args = (d["q"], d["k"], d["v"], d["a"], d["A_log"], d["dtb"], d["beta"])
+    o1, S1 = kda.chunk_fwd_scalar(*args, None, chunk=64)
+    o2, S2 = kda.chunk_fwd_scalar(*args, torch.zeros_like(d["state_in"]), chunk=64)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    ref_o, ref_S = kda.chunk_fwd_scalar(*args, d["state_in"], chunk=64)
+    st = d["state_in"].clone()
+    o3, S3 = kda.chunk_fwd_scalar(*args, st, chunk=64, state_out=st)
+    assert S3.data_ptr() == st.data_ptr() and torch.equal(S3, ref_S) and torch.equal(o3, ref_o)

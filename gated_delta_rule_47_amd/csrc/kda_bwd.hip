@@ -18,9 +18,12 @@
 //      dbeta = k . (dS e).  Nothing uses atomics, so results are deterministic.
 //
 // Thread layout of step 2: thread (a, b) holds rows 4a..4a+3 and value columns
-// 4b..4b+3 of the K x VT tile.  Sums over columns are lane exchanges (DPP moves) across
-// the CB lanes of a row block; sums over rows are lane exchanges inside the wave (DPP
-// moves and permlane swaps) plus one LDS exchange between the four waves per token.
+// 4b..4b+3 of the K x VT tile.  Each wave holds every row of CBW column blocks (lane =
+// RB * bw + a, b = CBW * wave + bw), so the sums over rows that each token needs are lane
+// exchanges inside one wave (DPP moves and permlane swaps) and no token waits for another
+// wave.  The per-row sums over columns (the dq, dk, dg and dS e partials) are summed over
+// the wave's columns the same way, kept in a double-buffered LDS ring for RING tokens and
+// added over the waves at one barrier per RING tokens.
 #include "kda_common.h"
 #include "kda_launch.h"
 
@@ -69,16 +72,20 @@ bwd_reverse_kernel(const float* __restrict__ q, const float* __restrict__ k, con
                    const float* __restrict__ d_state_out, const float* __restrict__ ckpt, float* __restrict__ scratch,
                    float* __restrict__ part, float* __restrict__ dv, float* __restrict__ dstate_in, int H, int T,
                    int V, int CK, int nck, int nvt) {
-  constexpr int CB = VT / 4, RB = K / 4, NTH = RB * CB;
-  static_assert(NTH <= 256, "tile too large for one workgroup");
+  constexpr int CB = VT / 4, RB = K / 4;
+  constexpr int CBW = CB < 64 / RB ? CB : 64 / RB;   // column blocks per wave
+  constexpr int NW = CB / CBW;                         // waves that hold the tile
+  constexpr int RING = 4;                              // tokens per partial-sum flush
+  static_assert(NW <= 4 && RB * CBW <= 64, "tile too large for one workgroup");
   __shared__ float sAl[CKMAX * K], sK[CKMAX * K], sQ[CKMAX * K];
   __shared__ float sV[CKMAX * VT], sDO[CKMAX * VT], sB[CKMAX];
-  __shared__ float sRed[2][2][4][VT];
+  __shared__ float sPart[2][RING][NW][4 * K];          // per-wave row partials of RING tokens
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool act = tid < NTH;
-  const int b = tid % CB;                 // every lane < CB of every wave names one column block
-  const int a = act ? tid / CB : 0;       // idle threads alias row block 0 and never store
+  const int bw = lane / RB;
+  const bool act = wave < NW && bw < CBW;
+  const int a = act ? lane % RB : 0;      // idle threads alias row block 0 and never store
+  const int b = act ? wave * CBW + bw : 0;
   const int bh = blockIdx.x / nvt, vt = blockIdx.x % nvt, h = bh % H, v0 = vt * VT;
   const int BH = gridDim.x / nvt;
   const float mult2 = gate_multiplier(A_log[h]) * kLog2e;
@@ -91,34 +98,25 @@ bwd_reverse_kernel(const float* __restrict__ q, const float* __restrict__ k, con
     for (int j = 0; j < 4; ++j)
       dS[i][j] = (act && d_state_out) ? d_state_out[((size_t)bh * K + 4 * a + i) * V + v0 + 4 * b + j] : 0.0f;
 
-  // Sum of per-thread column partials p[0..3] over all rows of the tile.
-  auto col_reduce2 = [&](float (&p)[4], float (&p2)[4], int parity) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p[j] = act ? p[j] : 0.0f;
-      p2[j] = act ? p2[j] : 0.0f;
-      p[j] = xor_sum(p[j], CB, 64);
-      p2[j] = xor_sum(p2[j], CB, 64);
-    }
-    if (lane < CB) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sRed[parity][0][wave][4 * b + j] = p[j];
-        sRed[parity][1][wave][4 * b + j] = p2[j];
-      }
-    }
+  // sums over the tile's rows (all in this wave) and over the wave's columns
+  auto row_sum = [&](float x) { return xor_sum(act ? x : 0.0f, 1, RB); };
+  auto col_sum = [&](float x) { return xor_sum(act ? x : 0.0f, RB, RB * CBW); };
+
+  // the ring: tokens of the current round go to half `ring` at slot 0, 1, ...; a flush adds
+  // the waves' partials of `cnt` tokens (slot d is token t_first - d) into the tile's rows
+  int ring = 0;
+  auto flush = [&](int cnt, size_t tok_first) {
     lds_barrier();
+    for (int idx = tid; idx < cnt * 4 * K; idx += 256) {
+      const int d = idx / (4 * K), r = idx % (4 * K);
+      float acc = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) { s0 += sRed[parity][0][w][4 * b + j]; s1 += sRed[parity][1][w][4 * b + j]; }
-      p[j] = s0;
-      p2[j] = s1;
+      for (int w = 0; w < NW; ++w) acc += sPart[ring][d][w][r];
+      part[(((size_t)vt * BH + bh) * T + tok_first - d) * 4 * K + r] = acc;
     }
+    ring ^= 1;
   };
 
-  int parity = 0;
   for (int ci = nck - 1; ci >= 0; --ci) {
     const int tc0 = ci * CK;
     const int n = min(CK, T - tc0);
@@ -148,15 +146,15 @@ bwd_reverse_kernel(const float* __restrict__ q, const float* __restrict__ k, con
 
     // forward recompute: the states after tokens 0..n-2 of this chunk
     for (int t = 0; t < n - 1; ++t) {
-      float rp[4] = {0.f, 0.f, 0.f, 0.f}, dummy[4] = {0.f, 0.f, 0.f, 0.f};
+      float rp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float al = sAl[t * K + 4 * a + i], kk = sK[t * K + 4 * a + i];
 #pragma unroll
         for (int j = 0; j < 4; ++j) { S[i][j] *= al; rp[j] += S[i][j] * kk; }
       }
-      col_reduce2(rp, dummy, parity);
-      parity ^= 1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rp[j] = row_sum(rp[j]);
       const float bt = sB[t];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -186,6 +184,7 @@ bwd_reverse_kernel(const float* __restrict__ q, const float* __restrict__ k, con
     };
     floatx4 Snext[4];
     load_prev(n - 1, Snext);
+    int slot = 0;
     for (int t = n - 1; t >= 0; --t) {
       const size_t tok = (size_t)bh * T + tc0 + t;
       float Sprev[4][4];                           // S_{t-1}, undecayed
@@ -216,8 +215,11 @@ bwd_reverse_kernel(const float* __restrict__ q, const float* __restrict__ k, con
           ep[j] += al[i] * Sprev[i][j] * kk[i];    // S'^T k, S' = diag(alpha) S_{t-1}
           dep[j] += dS[i][j] * kk[i];              // dS^T k
         }
-      col_reduce2(ep, dep, parity);
-      parity ^= 1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ep[j] = row_sum(ep[j]);
+        dep[j] = row_sum(dep[j]);
+      }
       float e[4], de[4], edo = 0.0f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -240,17 +242,17 @@ bwd_reverse_kernel(const float* __restrict__ q, const float* __restrict__ k, con
           dS[i][j] = dsd;
         }
       }
-      // sums over this tile's value columns
-      edo = xor_sum(act ? edo : 0.f, 1, CB);
+      // sums over this wave's value columns; the waves' sums are added at the flush
+      edo = col_sum(edo);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sdo[i] = xor_sum(sdo[i], 1, CB);
-        dse[i] = xor_sum(dse[i], 1, CB);
-        sde[i] = xor_sum(sde[i], 1, CB);
-        dgp[i] = xor_sum(dgp[i], 1, CB);
+        sdo[i] = col_sum(sdo[i]);
+        dse[i] = col_sum(dse[i]);
+        sde[i] = col_sum(sde[i]);
+        dgp[i] = col_sum(dgp[i]);
       }
-      if (act && b == 0) {
-        float* pp = part + (((size_t)vt * BH + bh) * T + tc0 + t) * 4 * K;
+      if (act && bw == 0) {
+        float* pp = sPart[ring][slot][wave];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int c = 4 * a + i;
@@ -268,6 +270,10 @@ bwd_reverse_kernel(const float* __restrict__ q, const float* __restrict__ k, con
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) dS[i][j] *= al[i];    // dS_{t-1} = diag(alpha) dS'
+      if (++slot == RING || t == 0) {
+        flush(slot, (size_t)tc0 + t + slot - 1);
+        slot = 0;
+      }
     }
   }
   if (act) {

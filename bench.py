@@ -46,10 +46,12 @@ KERNEL_SOURCES = ("kda_chunk_fwd_pc.h", "kda_common.h")
 KERNEL_NAME = "kda::chunk_fwd_pc_kernel<128,64,32,false>"
 
 
-def kernel_label(wl, scalar_gate=False) -> str:
+def kernel_label(wl, scalar_gate=False, paired=False) -> str:
     """The forward instance a kda_chunk_fwd call of this workload launches (the tiling rules
     of the library's forward plan)."""
     C = min(wl.chunk, 32)
+    if paired:
+        return "kda::chunk_fwd_px_kernel<%d,%s>" % (max(32, wl.K), str(scalar_gate).lower())
     if wl.dtype == "bf16":
         return "kda::chunk_fwd_pc_kernel<%d,%d,%d,%s>" % (max(32, wl.K), min(64, max(16, wl.V)), C,
                                                          str(scalar_gate).lower())
@@ -245,6 +247,9 @@ def main():
                     help="override the workload's chunk (16, 32 or 64) to compare block sizes; the default "
                          "line uses the workload's own")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--paired", action="store_true",
+                    help="pass kda_chunk_fwd a workspace: the two value-tile workgroups of a head share the gate "
+                         "and WY stages (bf16, V = 128)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_long.json"),
                     help="HBM traffic per launch measured by rocprofv3 counters (if present)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -313,10 +318,13 @@ def main():
     scale = kda.read_scale(wl.K)
 
     fwd = kda.chunk_fwd_scalar if args.scalar_gate else kda.chunk_fwd
+    # the paired forward's ring (bf16, V = 128): allocated once, outside the timed region
+    ws_bytes = 0 if not args.paired else kda.chunk_fwd_workspace_bytes(wl.B, wl.H, wl.T, wl.K, wl.V, wl.chunk, dt)
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
 
     def step():
         fwd(d["q"], d["k"], d["v"], d["z"], A_log, dt_bias, d["beta"], state_in, scale=scale, chunk=wl.chunk, out=o,
-            state_out=state_out)
+            state_out=state_out, workspace=workspace)
 
     for _ in range(args.warmup):
         step()
@@ -334,6 +342,8 @@ def main():
     kern_ms = [a.elapsed_time(b) for a, b in evs]
     if not (torch.isfinite(o[0, 0].float()).all() and torch.isfinite(state_out).all()):
         raise SystemExit("non-finite output")
+    if workspace is not None and kda.chunk_fwd_status(workspace) != 0:
+        raise SystemExit("the paired forward reported a failed exchange")
 
     ms_per_step = wall * 1e3 / args.steps
     avg_kernel_ms = float(np.mean(kern_ms))
@@ -351,7 +361,7 @@ def main():
             traffic = None
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": kernel_label(wl, args.scalar_gate),
+            "kernel": kernel_label(wl, args.scalar_gate, paired=workspace is not None),
             "algorithmic_bytes_per_launch": nbytes,
             "avg_kernel_ms": round(avg_kernel_ms, 4), "min_kernel_ms": round(float(np.min(kern_ms)), 4)}
     cpu = None

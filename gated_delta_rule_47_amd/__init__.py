@@ -17,8 +17,10 @@ import torch
 
 from . import _lib
 
-__all__ = ["KdaError", "read_scale", "gate", "chunk_fwd", "chunk_fwd_scalar", "recurrent_step", "recurrent_step_scalar", "chunk_bwd",
-           "chunk_bwd_workspace_bytes", "counters", "status_string", "library_path"]
+__all__ = ["KdaError", "read_scale", "gate", "chunk_fwd", "chunk_fwd_scalar", "chunk_fwd_workspace_bytes",
+           "chunk_fwd_status", "set_exchange_timeout_us", "recurrent_step", "recurrent_step_scalar", "chunk_bwd",
+           "chunk_bwd_workspace_bytes", "gate_bwd", "gate_bwd_workspace_bytes", "counters", "status_string",
+           "library_path"]
 
 
 class KdaError(RuntimeError):
@@ -77,6 +79,21 @@ def _check_f32(name, t, shape):
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
 
 
+def _check_out(name, t, shape, dtype, device):
+    """A caller-supplied output must have exactly the shape, dtype and device the kernels
+    write: the C ABI sees only a pointer and cannot check its size."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
 def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -112,28 +129,51 @@ def _check_acts(q, k, v, z, beta, scalar_gate=False):
     return B, H, T, K, V
 
 
+def chunk_fwd_workspace_bytes(B, H, T, K, V, chunk=64, dtype=torch.bfloat16) -> int:
+    """Workspace bytes kda_chunk_fwd can use (nonzero for bf16, V = 128, chunk 32/64)."""
+    code = _lib.KDA_BF16 if dtype == torch.bfloat16 else _lib.KDA_F32
+    return int(_lib.load().kda_chunk_fwd_workspace_bytes(B, H, T, K, V, chunk, code))
+
+
+def chunk_fwd_status(workspace) -> int:
+    """Synchronizes the current stream and returns (and clears) the status of the last
+    paired forward that used `workspace`: 0, or KDA_ERR_EXCHANGE (-9)."""
+    return int(_lib.load().kda_chunk_fwd_status(_ptr(workspace), _stream(workspace.device)))
+
+
+def set_exchange_timeout_us(us: int) -> None:
+    """Bound of the paired forward's waits in microseconds (0: give up at once)."""
+    _call("kda_set_exchange_timeout_us", ctypes.c_ulonglong(int(us)))
+
+
 def chunk_fwd(q, k, v, z, A_log, dt_bias, beta, state_in=None, scale=None, chunk=64,
-              output_state=True, out=None, state_out=None):
+              output_state=True, out=None, state_out=None, workspace=None):
     """Chunked KDA forward.  Returns (o, state_out); state_out is None when
-    output_state is False.  scale=None means K**-0.5."""
+    output_state is False.  scale=None means K**-0.5.  workspace: None runs without one
+    (each value tile computes every block's gate and WY stages), "auto" allocates the
+    buffer chunk_fwd_workspace_bytes() asks for (torch's caching allocator), or a uint8
+    CUDA tensor of at least that size (the paired path)."""
     return _chunk_fwd("kda_chunk_fwd", q, k, v, z, A_log, dt_bias, beta, state_in, scale, chunk, output_state,
-                      out, state_out)
+                      out, state_out, workspace)
 
 
 def chunk_fwd_scalar(q, k, v, a, A_log, dt_bias, beta, state_in=None, scale=None, chunk=64,
-                     output_state=True, out=None, state_out=None):
+                     output_state=True, out=None, state_out=None, workspace=None):
     """Chunked forward under a scalar decay: a (B,H,T) one gate input per token and
     head, dt_bias (H,) or None.  Otherwise as chunk_fwd."""
     return _chunk_fwd("kda_chunk_fwd_scalar", q, k, v, a, A_log, dt_bias, beta, state_in, scale, chunk,
-                      output_state, out, state_out)
+                      output_state, out, state_out, workspace)
 
 
-def _chunk_fwd(fn, q, k, v, z, A_log, dt_bias, beta, state_in, scale, chunk, output_state, out, state_out):
+def _chunk_fwd(fn, q, k, v, z, A_log, dt_bias, beta, state_in, scale, chunk, output_state, out, state_out,
+               workspace):
     scalar_gate = fn == "kda_chunk_fwd_scalar"
     B, H, T, K, V = _check_acts(q, k, v, z, beta, scalar_gate)
     _check_f32("A_log", A_log, (H,))
     _check_f32("dt_bias", dt_bias, (H,) if scalar_gate else (H, K))
     _check_f32("state_in", state_in, (B, H, K, V))
+    _check_out("out", out, (B, H, T, V), q.dtype, q.device)
+    _check_out("state_out", state_out, (B, H, K, V), torch.float32, q.device)
     if scale is None:
         scale = read_scale(K)
     o = out if out is not None else torch.empty((B, H, T, V), dtype=q.dtype, device=q.device)
@@ -141,9 +181,19 @@ def _chunk_fwd(fn, q, k, v, z, A_log, dt_bias, beta, state_in, scale, chunk, out
         state_out = torch.empty((B, H, K, V), dtype=torch.float32, device=q.device)
     if not output_state:
         state_out = None
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a tensor")
+        need = chunk_fwd_workspace_bytes(B, H, T, K, V, chunk, q.dtype)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    wbytes = 0
+    if workspace is not None:
+        if workspace.device != q.device:
+            raise ValueError("workspace is on %s, expected %s" % (workspace.device, q.device))
+        wbytes = workspace.numel() * workspace.element_size()
     _call(fn, _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(dt_bias), _ptr(beta),
-          _ptr(state_in), float(scale), int(chunk), _ptr(o), _ptr(state_out), B, H, T, K, V,
-          _dtype_code(q), _stream(q.device))
+          _ptr(state_in), float(scale), int(chunk), _ptr(o), _ptr(state_out), _ptr(workspace), wbytes,
+          B, H, T, K, V, _dtype_code(q), _stream(q.device))
     return o, state_out
 
 
@@ -172,6 +222,7 @@ def _recurrent_step(fn, q, k, v, z, A_log, dt_bias, beta, state, scale, out):
     _check_f32("A_log", A_log, (H,))
     _check_f32("dt_bias", dt_bias, (H,) if scalar_gate else (H, K))
     _check_f32("state", state, (B, H, K, V))
+    _check_out("out", out, (B, H, V), q.dtype, q.device)
     if scale is None:
         scale = read_scale(K)
     o = out if out is not None else torch.empty((B, H, V), dtype=q.dtype, device=q.device)
@@ -226,6 +277,7 @@ def gate_bwd(z, A_log, dt_bias, dg, want_dz=True, workspace=None, dz_out=None):
     _check_f32("dg", dg, (B, H, T, K))
     dev = z.device
     f32 = dict(dtype=torch.float32, device=dev)
+    _check_out("dz_out", dz_out, (B, H, T, K), torch.float32, dev)
     dz = (dz_out if dz_out is not None else torch.empty((B, H, T, K), **f32)) if want_dz else None
     dA = torch.empty((H,), **f32)
     ddb = torch.empty((H, K), **f32)

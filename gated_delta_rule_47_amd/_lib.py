@@ -11,7 +11,8 @@ KDA_OK = 0
 KDA_F32 = 0
 KDA_BF16 = 1
 COUNTER_NAMES = ("gate", "chunk_fwd", "recurrent_step", "chunk_bwd", "rejected", "gate_bwd")
-EXPORTED = ("kda_read_scale", "kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_scalar", "kda_recurrent_step",
+EXPORTED = ("kda_read_scale", "kda_gate", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_scalar",
+            "kda_chunk_fwd_status", "kda_set_exchange_timeout_us", "kda_recurrent_step",
             "kda_recurrent_step_scalar",
             "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_gate_bwd_workspace_bytes", "kda_gate_bwd",
             "kda_status_string", "kda_get_counters")
@@ -26,8 +27,12 @@ _sz = ctypes.c_size_t
 _PROTOS = {
     "kda_read_scale": (_f, [_i]),
     "kda_gate": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]),
-    "kda_chunk_fwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p, _p, _i, _i, _i, _i, _i, _i, _p]),
-    "kda_chunk_fwd_scalar": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p, _p, _i, _i, _i, _i, _i, _i, _p]),
+    "kda_chunk_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "kda_chunk_fwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p, _p, _p, _sz, _i, _i, _i, _i, _i, _i, _p]),
+    "kda_chunk_fwd_scalar": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p, _p, _p, _sz, _i, _i, _i, _i, _i, _i,
+                                  _p]),
+    "kda_chunk_fwd_status": (_i, [_p, _p]),
+    "kda_set_exchange_timeout_us": (_i, [ctypes.c_ulonglong]),
     "kda_recurrent_step": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _f, _p, _i, _i, _i, _i, _i, _p]),
     "kda_recurrent_step_scalar": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _f, _p, _i, _i, _i, _i, _i, _p]),
     "kda_chunk_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),

@@ -16,6 +16,12 @@ static int reject(int status) {
   return status;
 }
 
+// Bound of every wait for the partner workgroup, in 100 MHz real-time ticks (1 s).
+static std::atomic<unsigned long long> g_spin_ticks{100000000ull};
+
+// A bf16 call with two value tiles of 64 columns and blocks of 32 tokens runs paired.
+static bool px_eligible(bool bf16, int V, int chunk) { return bf16 && V == 128 && chunk >= 32; }
+
 static bool valid_dim(int d) { return d == 8 || d == 16 || d == 32 || d == 64 || d == 128; }
 static bool valid_chunk(int c) { return c == 16 || c == 32 || c == 64; }
 static size_t esize(int dtype) { return dtype == KDA_BF16 ? 2 : 4; }
@@ -99,6 +105,7 @@ const char* kda_status_string(int status) {
     case KDA_ERR_HIP: return "HIP launch or runtime error";
     case KDA_ERR_WORKSPACE: return "workspace missing or too small";
     case KDA_ERR_ALIGN: return "misaligned activation pointer";
+    case KDA_ERR_EXCHANGE: return "the two workgroups of a head failed to exchange blocks (outputs undefined)";
     default: return "unknown status";
   }
 }
@@ -133,8 +140,8 @@ int kda_gate(const void* z, const float* A_log, const float* dt_bias, float* g_o
 // z (B,H,T), dt_bias (H)): checks, then one launch.
 static int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* z, const float* A_log,
                           const float* dt_bias, const void* beta, const float* state_in, float scale, int chunk,
-                          void* o, float* state_out, int B, int H, int T, int K, int V, int dtype, void* stream,
-                          int zc) {
+                          void* o, float* state_out, void* workspace, size_t workspace_bytes, int B, int H, int T,
+                          int K, int V, int dtype, void* stream, int zc) {
   if (!A_log || (T != 0 && (!q || !k || !v || !z || !beta || !o))) return reject(KDA_ERR_NULL);
   if (dtype != KDA_F32 && dtype != KDA_BF16) return reject(KDA_ERR_DTYPE);
   if (B < 1 || H < 1 || T < 0 || !valid_dim(K) || !valid_dim(V)) return reject(KDA_ERR_SHAPE);
@@ -163,9 +170,37 @@ static int chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     return reject(KDA_ERR_ALIAS);
   FwdPlan plan;
   if (!fwd_plan(dtype == KDA_BF16, K, V, chunk, &plan)) return reject(KDA_ERR_SHAPE);
+  // paired path: needs the workspace (without one, each value tile recomputes the
+  // gate and WY stages of its head)
+  const bool paired = T > 0 && workspace && px_eligible(dtype == KDA_BF16, V, chunk);
+  if (paired) {
+    const size_t need = px_workspace_bytes(plan.KD, B * H);
+    if (workspace_bytes < need) return reject(KDA_ERR_WORKSPACE);
+    if ((uintptr_t)workspace & 255) return reject(KDA_ERR_ALIGN);
+    struct Buf { const void* p; size_t n; };
+    const Buf all[] = {{q, nk}, {k, nk}, {v, nv}, {z, nz}, {beta, nb}, {state_in, ns}, {o, nv}, {state_out, ns},
+                       {A_log, (size_t)H * 4}, {dt_bias, (size_t)H * (zc ? K : 1) * 4}};
+    for (const Buf& b : all)
+      if (overlap(workspace, need, b.p, b.n)) return reject(KDA_ERR_ALIAS);
+  }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
-  if (T == 0) {
+  if (paired) {
+    {
+      const unsigned long long spin = g_spin_ticks.load(std::memory_order_relaxed);
+#define KDA_FWD_PX(KD_)                                                                                        \
+  e = launch_chunk_fwd_px_kd<KD_>(q, k, v, z, A_log, dt_bias, beta, state_in, scale, o, state_out, B, H, T, K, zc, \
+                                  workspace, spin, s);                                                         \
+  break;
+      switch (plan.KD) {
+        case 32: KDA_FWD_PX(32)
+        case 64: KDA_FWD_PX(64)
+        case 128: KDA_FWD_PX(128)
+        default: e = hipErrorInvalidValue;
+      }
+#undef KDA_FWD_PX
+    }
+  } else if (T == 0) {
     if (state_out && state_out != state_in) {
       const long long n = (long long)B * H * K * V;
       hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, state_in, state_out,
@@ -206,18 +241,42 @@ static int recurrent_step_impl(const void* q, const void* k, const void* v, cons
 
 extern "C" {
 
+size_t kda_chunk_fwd_workspace_bytes(int B, int H, int T, int K, int V, int chunk, int dtype) {
+  if (B < 1 || H < 1 || T < 1 || !valid_dim(K) || !valid_dim(V) || !valid_chunk(chunk)) return 0;
+  if (!px_eligible(dtype == KDA_BF16, V, chunk)) return 0;
+  return px_workspace_bytes(K < 32 ? 32 : K, B * H);
+}
+
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* z, const float* A_log,
                   const float* dt_bias, const void* beta, const float* state_in, float scale, int chunk, void* o,
-                  float* state_out, int B, int H, int T, int K, int V, int dtype, void* stream) {
-  return chunk_fwd_impl(q, k, v, z, A_log, dt_bias, beta, state_in, scale, chunk, o, state_out, B, H, T, K, V, dtype,
-                        stream, 1);
+                  float* state_out, void* workspace, size_t workspace_bytes, int B, int H, int T, int K, int V,
+                  int dtype, void* stream) {
+  return chunk_fwd_impl(q, k, v, z, A_log, dt_bias, beta, state_in, scale, chunk, o, state_out, workspace,
+                        workspace_bytes, B, H, T, K, V, dtype, stream, 1);
 }
 
 int kda_chunk_fwd_scalar(const void* q, const void* k, const void* v, const void* a, const float* A_log,
                          const float* dt_bias, const void* beta, const float* state_in, float scale, int chunk,
-                         void* o, float* state_out, int B, int H, int T, int K, int V, int dtype, void* stream) {
-  return chunk_fwd_impl(q, k, v, a, A_log, dt_bias, beta, state_in, scale, chunk, o, state_out, B, H, T, K, V, dtype,
-                        stream, 0);
+                         void* o, float* state_out, void* workspace, size_t workspace_bytes, int B, int H, int T,
+                         int K, int V, int dtype, void* stream) {
+  return chunk_fwd_impl(q, k, v, a, A_log, dt_bias, beta, state_in, scale, chunk, o, state_out, workspace,
+                        workspace_bytes, B, H, T, K, V, dtype, stream, 0);
+}
+
+int kda_chunk_fwd_status(void* workspace, void* stream) {
+  if (!workspace) return reject(KDA_ERR_NULL);
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return KDA_ERR_HIP;
+  unsigned w = 0;
+  if (hipMemcpy(&w, workspace, 4, hipMemcpyDeviceToHost) != hipSuccess) return KDA_ERR_HIP;
+  if (w == 0) return KDA_OK;
+  const unsigned zero = 0;
+  if (hipMemcpy(workspace, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_ERR_EXCHANGE;
+}
+
+int kda_set_exchange_timeout_us(unsigned long long us) {
+  g_spin_ticks.store(us > (~0ull) / 100 ? ~0ull : us * 100, std::memory_order_relaxed);
+  return KDA_OK;
 }
 
 int kda_recurrent_step(const void* q, const void* k, const void* v, const void* z, const float* A_log,

@@ -42,6 +42,15 @@ hipError_t launch_chunk_fwd_pc_kd(int VT, int C, const void* q, const void* k, c
                                   float scale, void* o, float* state_out, int B, int H, int T, int K, int V, int zc,
                                   hipStream_t s);
 
+// Paired bf16 forward for V = 128 (two workgroups per head share the gate and WY work
+// through a ring in `work`, px_workspace_bytes() of it; see kda_chunk_fwd_px.h).
+template <int KD>
+hipError_t launch_chunk_fwd_px_kd(const void* q, const void* k, const void* v, const void* z, const float* A_log,
+                                  const float* dt_bias, const void* beta, const float* state_in, float scale, void* o,
+                                  float* state_out, int B, int H, int T, int K, int zc, void* work,
+                                  unsigned long long spin_ticks, hipStream_t s);
+size_t px_workspace_bytes(int KD, int nheads);
+
 // Forward tiling actually used for (dtype, K, V, chunk): padded key dim, value tile
 // and the chunk the kernel blocks by.  Returns false when no instance exists.
 struct FwdPlan {

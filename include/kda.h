@@ -23,7 +23,9 @@
  *     v, z, beta and of the output o.  States, A_log, dt_bias, g, alpha and all
  *     gradients are float32 whatever `dtype` is.
  *   - Every pointer is a device pointer.  The caller allocates and owns every
- *     buffer; the library keeps nothing between calls and allocates nothing.
+ *     buffer, workspaces included; the library allocates nothing.  Between calls it
+ *     keeps only process-wide counters and settings (kda_get_counters,
+ *     kda_set_exchange_timeout_us) and a launch counter of the paired forward.
  *     When T = 0, pointers to buffers with a T dimension may be NULL.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously on it; a call returns once its kernels are launched.
@@ -54,7 +56,10 @@ typedef enum {
   KDA_ERR_ALIAS = -5,      /* an output buffer aliases an input it must not alias */
   KDA_ERR_HIP = -6,        /* a HIP launch or runtime call failed */
   KDA_ERR_WORKSPACE = -7,  /* workspace NULL or smaller than kda_chunk_bwd_workspace_bytes() */
-  KDA_ERR_ALIGN = -8       /* an activation pointer (or kda_chunk_bwd's workspace) is misaligned */
+  KDA_ERR_ALIGN = -8,      /* an activation pointer or a workspace is misaligned */
+  KDA_ERR_EXCHANGE = -9    /* kda_chunk_fwd_status: the two workgroups of a head failed to hand
+                              blocks to each other (a bounded wait ran out, or they were not on
+                              one XCD); that call's outputs are undefined */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -74,6 +79,12 @@ int kda_gate(const void* z, const float* A_log, const float* dt_bias,
              float* g_out, float* alpha_out,
              int B, int H, int T, int K, int dtype, void* stream);
 
+/* Bytes of device workspace kda_chunk_fwd / kda_chunk_fwd_scalar can use for these
+ * sizes: nonzero for KDA_BF16 with V = 128 and chunk 32 or 64 (the paired path below),
+ * 0 for every other call (and on bad sizes).  It grows with B*H up to 128 heads and
+ * stays constant beyond (about 27.6 MB at K = 128). */
+size_t kda_chunk_fwd_workspace_bytes(int B, int H, int T, int K, int V, int chunk, int dtype);
+
 /* Chunked KDA forward: the gate, the read-scale fold, the intra-chunk WY stage
  * (decay-weighted strictly-lower beta k k^T, (I+A)^-1 by forward substitution,
  * w and u), the inter-chunk state passing and the output, fused in one kernel.
@@ -92,13 +103,40 @@ int kda_gate(const void* z, const float* A_log, const float* dt_bias,
  *   o         (B,H,T,V) `dtype`; must not alias any input
  *   state_out (B,H,K,V) f32 final state, or NULL (not written); may equal state_in
  *             (each state tile is read before it is written by the same workgroup).
+ *   workspace device buffer of at least kda_chunk_fwd_workspace_bytes() bytes, 256-byte
+ *             aligned, or NULL.  When that size is nonzero and a workspace is given, the
+ *             two value tiles of each head run as a pair of workgroups that compute the
+ *             gate and WY stages of alternate blocks once and hand them to each other
+ *             through the workspace (L2 of their shared XCD); with NULL, or when the size
+ *             is 0, each value tile computes them itself (same results up to rounding,
+ *             slower).  Contents on entry are ignored; it must not overlap any other
+ *             argument (KDA_ERR_ALIAS), and two calls in flight at once must not share
+ *             one (their hand-offs would mix).  A too small workspace gives
+ *             KDA_ERR_WORKSPACE, a misaligned one KDA_ERR_ALIGN.  The pair's waits
+ *             are bounded (kda_set_exchange_timeout_us); if one runs out the call
+ *             still completes, its outputs are undefined and kda_chunk_fwd_status
+ *             reports KDA_ERR_EXCHANGE.
  * Matrix products run on MFMA: bf16 operands with fp32 accumulation for
  * KDA_BF16, fp32 operands for KDA_F32.  The state is carried in fp32. */
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* z,
                   const float* A_log, const float* dt_bias, const void* beta,
                   const float* state_in, float scale, int chunk,
                   void* o, float* state_out,
+                  void* workspace, size_t workspace_bytes,
                   int B, int H, int T, int K, int V, int dtype, void* stream);
+
+/* Outcome of the last paired kda_chunk_fwd / kda_chunk_fwd_scalar call that used this
+ * workspace: synchronizes `stream`, reads the workspace's status word and clears it.
+ * KDA_OK, or KDA_ERR_EXCHANGE when a wait between the workgroups of a head ran out or
+ * they were not placed on one XCD (that call's outputs are undefined); KDA_ERR_HIP if
+ * the synchronization or the copy fails. */
+int kda_chunk_fwd_status(void* workspace, void* stream);
+
+/* Bound of each wait of the paired forward for the other workgroup of its head, in
+ * microseconds (default 1000000).  0 makes every such wait give up at once, which
+ * exercises the failure path (the call then reports KDA_ERR_EXCHANGE).  Process-wide;
+ * takes effect for calls made after it.  Returns KDA_OK. */
+int kda_set_exchange_timeout_us(unsigned long long us);
 
 /* One decode step of the same recurrence (the page's "decode prefill read" folds
  * the scale into q the same way).  Inputs are one token per (b,h):
@@ -125,6 +163,7 @@ int kda_chunk_fwd_scalar(const void* q, const void* k, const void* v, const void
                          const float* A_log, const float* dt_bias, const void* beta,
                          const float* state_in, float scale, int chunk,
                          void* o, float* state_out,
+                         void* workspace, size_t workspace_bytes,
                          int B, int H, int T, int K, int V, int dtype, void* stream);
 
 /* Decode step under the scalar decay: as kda_recurrent_step with a (B,H) `dtype` (one

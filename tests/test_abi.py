@@ -47,8 +47,8 @@ def test_read_scale():
 def test_status_strings_and_counters():
     lib = _lib()
     assert lib.kda_status_string(0) == b"ok"
-    names = {lib.kda_status_string(s) for s in range(-8, 1)}
-    assert len(names) == 9 and b"unknown status" not in names
+    names = {lib.kda_status_string(s) for s in range(-9, 1)}
+    assert len(names) == 10 and b"unknown status" not in names
     assert lib.kda_status_string(-99) == b"unknown status"
     n = lib.kda_get_counters(None, 0)
     arr = (ctypes.c_ulonglong * n)()
@@ -65,6 +65,16 @@ def test_workspace_bytes():
     assert lib.kda_gate_bwd_workspace_bytes(2, 3, 300, 8) == 2 * 3 * 2 * 2 * 8 * 4
     assert lib.kda_gate_bwd_workspace_bytes(1, 1, 0, 8) == 0
     assert lib.kda_gate_bwd_workspace_bytes(1, 1, 16, 0) == 0
+    # paired forward: bf16 with V = 128 and chunk 32/64 only; one ring per head up to 128
+    fw = lib.kda_chunk_fwd_workspace_bytes
+    one = fw(1, 1, 64, 128, 128, 64, 1)
+    assert one > 6 * 35 * 1024 and fw(4, 32, 16384, 128, 128, 64, 1) == 256 + 128 * (one - 256)
+    assert fw(8, 32, 64, 128, 128, 64, 1) == fw(4, 32, 64, 128, 128, 64, 1)
+    assert fw(1, 1, 64, 128, 128, 32, 1) == one
+    assert fw(1, 1, 64, 64, 128, 64, 1) < one and fw(1, 1, 64, 8, 128, 64, 1) == fw(1, 1, 64, 32, 128, 64, 1) > 0
+    for args in ((1, 1, 64, 128, 128, 16, 1), (1, 1, 64, 128, 64, 64, 1), (1, 1, 64, 128, 128, 64, 0),
+                 (1, 1, 0, 128, 128, 64, 1), (0, 1, 64, 128, 128, 64, 1), (1, 1, 64, 128, 96, 64, 1)):
+        assert fw(*args) == 0, args
 
 
 def _gpu_visible():
@@ -84,26 +94,26 @@ def test_argument_errors_before_launch():
     rej0 = (ctypes.c_ulonglong * 6)()
     lib.kda_get_counters(rej0, 6)
     # null input
-    assert lib.kda_chunk_fwd(None, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 8, 0, None) == -1
+    assert lib.kda_chunk_fwd(None, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, None, 0, 1, 1, 16, 8, 8, 0, None) == -1
     # bad dtype
-    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 8, 7, None) == -3
+    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, None, 0, 1, 1, 16, 8, 8, 7, None) == -3
     # bad shapes
-    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 12, 8, 0, None) == -2
-    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, 0, 1, 16, 8, 8, 0, None) == -2
-    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, -1, 8, 8, 0, None) == -2
+    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, None, 0, 1, 1, 16, 12, 8, 0, None) == -2
+    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, None, 0, 0, 1, 16, 8, 8, 0, None) == -2
+    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, None, 0, 1, 1, -1, 8, 8, 0, None) == -2
     # one head's sequence too long for 32-bit offsets (2^31 / (128 * 2) tokens, bf16)
-    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 1 << 23, 128, 128, 1,
+    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, None, 0, 1, 1, 1 << 23, 128, 128, 1,
                              None) == -2
     # bad chunk
-    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 48, o, s_out, 1, 1, 16, 8, 8, 0, None) == -4
+    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 48, o, s_out, None, 0, 1, 1, 16, 8, 8, 0, None) == -4
     # activation pointer not aligned to two elements
-    assert lib.kda_chunk_fwd(q, P(0x20002), v, z, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 8, 1,
+    assert lib.kda_chunk_fwd(q, P(0x20002), v, z, A, dt, b, s_in, 0.1, 64, o, s_out, None, 0, 1, 1, 16, 8, 8, 1,
                              None) == -8
-    assert lib.kda_chunk_fwd(q, k, v, P(0x40004), A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 8, 0,
+    assert lib.kda_chunk_fwd(q, k, v, P(0x40004), A, dt, b, s_in, 0.1, 64, o, s_out, None, 0, 1, 1, 16, 8, 8, 0,
                              None) == -8
     # output aliasing an input
-    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, q, s_out, 1, 1, 16, 8, 8, 0, None) == -5
-    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, k, 1, 1, 16, 8, 8, 0, None) == -5
+    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, q, s_out, None, 0, 1, 1, 16, 8, 8, 0, None) == -5
+    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, k, None, 0, 1, 1, 16, 8, 8, 0, None) == -5
     # decode step
     assert lib.kda_recurrent_step(q, k, v, z, A, dt, b, None, 0.1, o, 1, 1, 8, 8, 0, None) == -1
     assert lib.kda_recurrent_step(q, k, v, z, A, dt, b, s_in, 0.1, o, 1, 1, 8, 24, 0, None) == -2
@@ -143,16 +153,16 @@ def test_scalar_decay_argument_errors_before_launch():
     rej0 = (ctypes.c_ulonglong * 6)()
     lib.kda_get_counters(rej0, 6)
     f = lib.kda_chunk_fwd_scalar
-    assert f(q, k, v, None, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 8, 1, None) == -1
-    assert f(q, k, v, a, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 8, 9, None) == -3
-    assert f(q, k, v, a, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 24, 1, None) == -2
-    assert f(q, k, v, a, A, dt, b, s_in, 0.1, 8, o, s_out, 1, 1, 16, 8, 8, 1, None) == -4
+    assert f(q, k, v, None, A, dt, b, s_in, 0.1, 64, o, s_out, None, 0, 1, 1, 16, 8, 8, 1, None) == -1
+    assert f(q, k, v, a, A, dt, b, s_in, 0.1, 64, o, s_out, None, 0, 1, 1, 16, 8, 8, 9, None) == -3
+    assert f(q, k, v, a, A, dt, b, s_in, 0.1, 64, o, s_out, None, 0, 1, 1, 16, 8, 24, 1, None) == -2
+    assert f(q, k, v, a, A, dt, b, s_in, 0.1, 8, o, s_out, None, 0, 1, 1, 16, 8, 8, 1, None) == -4
     # the gate input needs one-element alignment only; q, k, v keep the two-element rule
-    assert f(q, k, v, P(0x40001), A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 8, 1, None) == -8
-    assert f(q, P(0x20002), v, a, A, dt, b, s_in, 0.1, 64, o, s_out, 1, 1, 16, 8, 8, 1, None) == -8
+    assert f(q, k, v, P(0x40001), A, dt, b, s_in, 0.1, 64, o, s_out, None, 0, 1, 1, 16, 8, 8, 1, None) == -8
+    assert f(q, P(0x20002), v, a, A, dt, b, s_in, 0.1, 64, o, s_out, None, 0, 1, 1, 16, 8, 8, 1, None) == -8
     # o or state_out over the gate input (B*H*T elements)
-    assert f(q, k, v, a, A, dt, b, s_in, 0.1, 64, P(a.value + 2), s_out, 1, 1, 16, 8, 8, 1, None) == -5
-    assert f(q, k, v, a, A, dt, b, s_in, 0.1, 64, o, P(a.value - 4), 1, 1, 16, 8, 8, 0, None) == -5
+    assert f(q, k, v, a, A, dt, b, s_in, 0.1, 64, P(a.value + 2), s_out, None, 0, 1, 1, 16, 8, 8, 1, None) == -5
+    assert f(q, k, v, a, A, dt, b, s_in, 0.1, 64, o, P(a.value - 4), None, 0, 1, 1, 16, 8, 8, 0, None) == -5
     g = lib.kda_recurrent_step_scalar
     assert g(q, k, v, None, A, dt, b, s_in, 0.1, o, 1, 1, 8, 8, 0, None) == -1
     assert g(q, k, v, a, A, dt, b, s_in, 0.1, o, 1, 1, 8, 12, 0, None) == -2
@@ -160,3 +170,37 @@ def test_scalar_decay_argument_errors_before_launch():
     rej1 = (ctypes.c_ulonglong * 6)()
     lib.kda_get_counters(rej1, 6)
     assert rej1[4] - rej0[4] == 11 and list(rej1[:4]) == list(rej0[:4])
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake device pointers: CPU-only check")
+def test_paired_forward_workspace_errors_before_launch():
+    lib = _lib()
+    P = ctypes.c_void_p
+    q, k, v, z, A, dt, b, s_in, o, s_out = [P(0x1000000 * (i + 1)) for i in range(10)]
+    need = lib.kda_chunk_fwd_workspace_bytes(1, 2, 64, 128, 128, 64, 1)
+    ws = P(0x40000000)
+    rej0 = (ctypes.c_ulonglong * 6)()
+    lib.kda_get_counters(rej0, 6)
+    f = lib.kda_chunk_fwd
+    # too small, misaligned, overlapping an input or an output
+    assert f(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, ws, need - 1, 1, 2, 64, 128, 128, 1, None) == -7
+    assert f(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, P(ws.value + 16), need, 1, 2, 64, 128, 128, 1,
+             None) == -8
+    assert f(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, P(v.value - 256), need, 1, 2, 64, 128, 128, 1,
+             None) == -5
+    assert f(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, P(s_out.value - 256), need, 1, 2, 64, 128, 128, 1,
+             None) == -5
+    assert f(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, s_out, P(A.value), need, 1, 2, 64, 128, 128, 1,
+             None) == -5
+    g = lib.kda_chunk_fwd_scalar
+    assert g(q, k, v, z, A, dt, b, s_in, 0.1, 32, o, s_out, ws, 100, 1, 2, 64, 128, 128, 1, None) == -7
+    assert lib.kda_chunk_fwd_status(None, None) == -1
+    rej1 = (ctypes.c_ulonglong * 6)()
+    lib.kda_get_counters(rej1, 6)
+    assert rej1[4] - rej0[4] == 7 and list(rej1[:4]) == list(rej0[:4])
+
+
+def test_exchange_timeout_setting():
+    lib = _lib()
+    assert lib.kda_set_exchange_timeout_us(0) == 0
+    assert lib.kda_set_exchange_timeout_us(1000000) == 0

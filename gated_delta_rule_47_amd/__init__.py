@@ -19,7 +19,8 @@ from . import _lib
 
 __all__ = ["KdaError", "read_scale", "gate", "chunk_fwd", "chunk_fwd_scalar", "chunk_fwd_workspace_bytes",
            "chunk_fwd_status", "set_exchange_timeout_us", "recurrent_step", "recurrent_step_scalar", "chunk_bwd",
-           "chunk_bwd_workspace_bytes", "gate_bwd", "gate_bwd_workspace_bytes", "counters", "status_string",
+           "chunk_bwd_workspace_bytes", "gate_bwd", "gate_bwd_workspace_bytes", "gate_bwd_noalloc",
+           "GATE_BWD_SCRATCH_BYTES", "counters", "status_string",
            "library_path"]
 
 
@@ -286,4 +287,30 @@ def gate_bwd(z, A_log, dt_bias, dg, want_dz=True, workspace=None, dz_out=None):
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _call("kda_gate_bwd", _ptr(z), _ptr(A_log), _ptr(dt_bias), _ptr(dg), _ptr(dz), _ptr(dA), _ptr(ddb),
           _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, T, K, _dtype_code(z), _stream(dev))
+    return dz, dA, ddb
+
+
+# Bytes of the library's built-in scratch that gate_bwd_noalloc uses (per GPU).
+GATE_BWD_SCRATCH_BYTES = 16 << 20
+
+
+def gate_bwd_noalloc(z, A_log, dt_bias, dg, dz_out=None, dA_out=None, ddb_out=None, want_dz=True):
+    """gate_bwd through the entry point that allocates no device memory: the partial sums
+    live in the library's per-GPU scratch (sizes needing more than GATE_BWD_SCRATCH_BYTES
+    are rejected).  Outputs are allocated here unless given; calls that may overlap on one
+    GPU (unordered streams) race on the scratch."""
+    B, H, T, K = z.shape
+    _check_f32("A_log", A_log, (H,))
+    _check_f32("dt_bias", dt_bias, (H, K))
+    _check_f32("dg", dg, (B, H, T, K))
+    dev = z.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    _check_out("dz_out", dz_out, (B, H, T, K), torch.float32, dev)
+    _check_out("dA_out", dA_out, (H,), torch.float32, dev)
+    _check_out("ddb_out", ddb_out, (H, K), torch.float32, dev)
+    dz = (dz_out if dz_out is not None else torch.empty((B, H, T, K), **f32)) if want_dz else None
+    dA = dA_out if dA_out is not None else torch.empty((H,), **f32)
+    ddb = ddb_out if ddb_out is not None else torch.empty((H, K), **f32)
+    _call("kda_gate_bwd_noalloc", _ptr(z), _ptr(A_log), _ptr(dt_bias), _ptr(dg), _ptr(dz), _ptr(dA), _ptr(ddb),
+          B, H, T, K, _dtype_code(z), _stream(dev))
     return dz, dA, ddb

@@ -14,7 +14,7 @@ COUNTER_NAMES = ("gate", "chunk_fwd", "recurrent_step", "chunk_bwd", "rejected",
 EXPORTED = ("kda_read_scale", "kda_gate", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_scalar",
             "kda_chunk_fwd_status", "kda_set_exchange_timeout_us", "kda_recurrent_step",
             "kda_recurrent_step_scalar",
-            "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_gate_bwd_workspace_bytes", "kda_gate_bwd",
+            "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_gate_bwd_workspace_bytes", "kda_gate_bwd", "kda_gate_bwd_noalloc",
             "kda_status_string", "kda_get_counters")
 
 _lib = None
@@ -40,6 +40,7 @@ _PROTOS = {
                            _i, _i, _i, _i, _i, _i, _p]),
     "kda_gate_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "kda_gate_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _sz, _i, _i, _i, _i, _i, _p]),
+    "kda_gate_bwd_noalloc": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "kda_status_string": (ctypes.c_char_p, [_i]),
     "kda_get_counters": (_i, [ctypes.POINTER(ctypes.c_ulonglong), _i]),
 }

@@ -106,6 +106,7 @@ const char* kda_status_string(int status) {
     case KDA_ERR_WORKSPACE: return "workspace missing or too small";
     case KDA_ERR_ALIGN: return "misaligned activation pointer";
     case KDA_ERR_EXCHANGE: return "the two workgroups of a head failed to exchange blocks (outputs undefined)";
+    case KDA_ERR_SCRATCH: return "sizes need more than the built-in scratch of the allocation-free call";
     default: return "unknown status";
   }
 }
@@ -334,14 +335,22 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z, co
 
 size_t kda_gate_bwd_workspace_bytes(int B, int H, int T, int K) { return gate_bwd_workspace_bytes(B, H, T, K); }
 
-int kda_gate_bwd(const void* z, const float* A_log, const float* dt_bias, const float* dg, float* dz, float* dA_log,
-                 float* d_dt_bias, void* workspace, size_t workspace_bytes, int B, int H, int T, int K, int dtype,
-                 void* stream) {
+}  // extern "C"
+
+// Checks of kda_gate_bwd and kda_gate_bwd_noalloc, then the launch.  `workspace` is
+// the caller's buffer or the built-in scratch (need bytes of either are used).
+static int gate_bwd_impl(const void* z, const float* A_log, const float* dt_bias, const float* dg, float* dz,
+                         float* dA_log, float* d_dt_bias, bool noalloc, void* workspace, size_t workspace_bytes,
+                         int B, int H, int T, int K, int dtype, void* stream) {
   if (!A_log || (!dz && !dA_log && !d_dt_bias) || (T != 0 && (!z || !dg))) return reject(KDA_ERR_NULL);
   if (dtype != KDA_F32 && dtype != KDA_BF16) return reject(KDA_ERR_DTYPE);
   if (B < 1 || H < 1 || T < 0 || K < 1) return reject(KDA_ERR_SHAPE);
   const size_t need = gate_bwd_workspace_bytes(B, H, T, K);
-  if (need && (!workspace || workspace_bytes < need)) return reject(KDA_ERR_WORKSPACE);
+  if (noalloc) {
+    if (need > KDA_GATE_BWD_SCRATCH_BYTES) return reject(KDA_ERR_SCRATCH);
+  } else if (need && (!workspace || workspace_bytes < need)) {
+    return reject(KDA_ERR_WORKSPACE);
+  }
   const size_t n = (size_t)B * H * T * K;
   struct Buf { const void* p; size_t n; };
   const Buf ins[] = {{z, n * esize(dtype)}, {A_log, (size_t)H * 4}, {dt_bias, (size_t)H * K * 4}, {workspace, need}};
@@ -357,6 +366,7 @@ int kda_gate_bwd(const void* z, const float* A_log, const float* dt_bias, const 
   if ((dz != dg && overlap(dz, n * 4, dg, n * 4)) || overlap(dA_log, (size_t)H * 4, dg, n * 4) ||
       overlap(d_dt_bias, (size_t)H * K * 4, dg, n * 4))
     return reject(KDA_ERR_ALIAS);
+  if (noalloc && need && gate_bwd_scratch(&workspace) != hipSuccess) return reject(KDA_ERR_HIP);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dtype == KDA_BF16
                      ? launch_gate_bwd<bf16_t>(z, A_log, dt_bias, dg, dz, dA_log, d_dt_bias, workspace, B, H, T, K, s)
@@ -364,6 +374,20 @@ int kda_gate_bwd(const void* z, const float* A_log, const float* dt_bias, const 
   if (e != hipSuccess) return reject(KDA_ERR_HIP);
   g_counters[KDA_COUNTER_GATE_BWD].fetch_add(1, std::memory_order_relaxed);
   return KDA_OK;
+}
+
+extern "C" {
+
+int kda_gate_bwd(const void* z, const float* A_log, const float* dt_bias, const float* dg, float* dz, float* dA_log,
+                 float* d_dt_bias, void* workspace, size_t workspace_bytes, int B, int H, int T, int K, int dtype,
+                 void* stream) {
+  return gate_bwd_impl(z, A_log, dt_bias, dg, dz, dA_log, d_dt_bias, false, workspace, workspace_bytes, B, H, T, K,
+                       dtype, stream);
+}
+
+int kda_gate_bwd_noalloc(const void* z, const float* A_log, const float* dt_bias, const float* dg, float* dz,
+                         float* dA_log, float* d_dt_bias, int B, int H, int T, int K, int dtype, void* stream) {
+  return gate_bwd_impl(z, A_log, dt_bias, dg, dz, dA_log, d_dt_bias, true, nullptr, 0, B, H, T, K, dtype, stream);
 }
 
 }  // extern "C"

@@ -12,6 +12,9 @@
 // contiguous VTS*4-byte segment.  The two reductions over K (the delta read
 // S'^T k and the output S^T q_hat) are a per-thread partial sum over its rows
 // followed by one LDS exchange between the NRG row groups.
+#include <mutex>
+
+#include "../../include/kda.h"
 #include "kda_common.h"
 #include "kda_launch.h"
 
@@ -196,6 +199,33 @@ hipError_t launch_gate(const void* z, const float* A_log, const float* dt_bias, 
   hipLaunchKernelGGL(gate_kernel<Tin>, dim3((unsigned)blocks), dim3(256), 0, s, (const Tin*)z, A_log, dt_bias, g,
                      alpha, H, T, K, n);
   return hipGetLastError();
+}
+
+// The gate adjoint's partial sums for callers that cannot allocate: a file-scope
+// device array (each GPU the library runs on holds its own copy until the process
+// ends).  Its name is only a host-side handle; kernels get the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[KDA_GATE_BWD_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+hipError_t gate_bwd_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 size_t gate_bwd_workspace_bytes(int B, int H, int T, int K) {

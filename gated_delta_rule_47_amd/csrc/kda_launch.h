@@ -14,6 +14,9 @@ hipError_t launch_gate(const void* z, const float* A_log, const float* dt_bias, 
 
 // Gate adjoint: dz (nullable), dA_log and d_dt_bias (nullable) for a cotangent dg.
 size_t gate_bwd_workspace_bytes(int B, int H, int T, int K);
+// Device address of the current device's built-in gate-adjoint scratch
+// (KDA_GATE_BWD_SCRATCH_BYTES), looked up once per device.
+hipError_t gate_bwd_scratch(void** ptr);
 template <typename Tin>
 hipError_t launch_gate_bwd(const void* z, const float* A_log, const float* dt_bias, const float* dg, float* dz,
                            float* dA_log, float* d_dt_bias, void* workspace, int B, int H, int T, int K,

@@ -57,9 +57,11 @@ typedef enum {
   KDA_ERR_HIP = -6,        /* a HIP launch or runtime call failed */
   KDA_ERR_WORKSPACE = -7,  /* workspace NULL or smaller than kda_chunk_bwd_workspace_bytes() */
   KDA_ERR_ALIGN = -8,      /* an activation pointer or a workspace is misaligned */
-  KDA_ERR_EXCHANGE = -9    /* kda_chunk_fwd_status: the two workgroups of a head failed to hand
+  KDA_ERR_EXCHANGE = -9,   /* kda_chunk_fwd_status: the two workgroups of a head failed to hand
                               blocks to each other (a bounded wait ran out, or they were not on
                               one XCD); that call's outputs are undefined */
+  KDA_ERR_SCRATCH = -10    /* kda_gate_bwd_noalloc: these sizes need more than the library's
+                              built-in scratch (KDA_GATE_BWD_SCRATCH_BYTES) */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -216,6 +218,23 @@ int kda_gate_bwd(const void* z, const float* A_log, const float* dt_bias, const 
                  float* dz, float* dA_log, float* d_dt_bias,
                  void* workspace, size_t workspace_bytes,
                  int B, int H, int T, int K, int dtype, void* stream);
+
+/* Bytes of the device array kda_gate_bwd_noalloc uses in place of a workspace (per GPU). */
+#define KDA_GATE_BWD_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* kda_gate_bwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, hosts that forbid it).  The
+ * per-tile partial sums go to a 16 MiB array inside the library, one per GPU, resident
+ * until the process ends; this call allocates nothing.  Same arguments, outputs, checks
+ * and results as kda_gate_bwd (bit-identical).  Sizes whose kda_gate_bwd_workspace_bytes()
+ * exceeds KDA_GATE_BWD_SCRATCH_BYTES give KDA_ERR_SCRATCH before anything runs.  `stream`
+ * must belong to the current device.  Every call on a GPU shares that GPU's array: two
+ * calls that may run at the same time on one GPU (different streams, no ordering between
+ * them) race and must not be made; calls in one stream are ordered and safe.  Nothing in
+ * the array needs to start at zero (every partial sum is written before it is read). */
+int kda_gate_bwd_noalloc(const void* z, const float* A_log, const float* dt_bias, const float* dg,
+                         float* dz, float* dA_log, float* d_dt_bias,
+                         int B, int H, int T, int K, int dtype, void* stream);
 
 /* Static string for a status code ("ok", "null pointer", ...). Never NULL. */
 const char* kda_status_string(int status);

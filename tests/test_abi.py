@@ -47,8 +47,8 @@ def test_read_scale():
 def test_status_strings_and_counters():
     lib = _lib()
     assert lib.kda_status_string(0) == b"ok"
-    names = {lib.kda_status_string(s) for s in range(-9, 1)}
-    assert len(names) == 10 and b"unknown status" not in names
+    names = {lib.kda_status_string(s) for s in range(-10, 1)}
+    assert len(names) == 11 and b"unknown status" not in names
     assert lib.kda_status_string(-99) == b"unknown status"
     n = lib.kda_get_counters(None, 0)
     arr = (ctypes.c_ulonglong * n)()
@@ -140,9 +140,19 @@ def test_argument_errors_before_launch():
     assert lib.kda_gate_bwd(z, A, dt, g[0], o, dt, None, ws, 1 << 20, 1, 1, 16, 8, 0, None) == -5
     assert lib.kda_gate_bwd(z, A, dt, g[0], P(g[0].value + 4), None, None, ws, 1 << 20, 1, 1, 16, 8, 0,
                             None) == -5
+    # the allocation-free gate adjoint: the same checks, and sizes beyond its built-in
+    # scratch (16 MiB of partial sums: 256 heads x 64 tiles x 2 x 128 channels x 4 B fit,
+    # 257 heads do not) rejected before anything runs
+    assert lib.kda_gate_bwd_noalloc(None, A, dt, g[0], o, None, None, 1, 1, 16, 8, 0, None) == -1
+    assert lib.kda_gate_bwd_noalloc(z, A, dt, g[0], o, None, None, 1, 1, 16, 8, 5, None) == -3
+    assert lib.kda_gate_bwd_noalloc(z, A, dt, g[0], o, None, None, 1, 1, 16, 0, 0, None) == -2
+    assert lib.kda_gate_bwd_noalloc(z, A, dt, g[0], z, None, None, 1, 1, 16, 8, 0, None) == -5
+    assert lib.kda_gate_bwd_workspace_bytes(1, 256, 16384, 128) == 16 << 20
+    assert lib.kda_gate_bwd_noalloc(z, A, dt, g[0], o, None, None, 1, 257, 16384, 128, 0, None) == -10
+    assert lib.kda_gate_bwd_noalloc(z, A, dt, g[0], o, None, None, 2, 1, 16384 * 128 + 1, 128, 0, None) == -10
     rej1 = (ctypes.c_ulonglong * 6)()
     lib.kda_get_counters(rej1, 6)
-    assert rej1[4] - rej0[4] == 29 and list(rej1[:4]) == list(rej0[:4]) and rej1[5] == rej0[5]
+    assert rej1[4] - rej0[4] == 35 and list(rej1[:4]) == list(rej0[:4]) and rej1[5] == rej0[5]
 
 
 @pytest.mark.skipif(_gpu_visible(), reason="fake device pointers: CPU-only check")

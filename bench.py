@@ -91,6 +91,43 @@ def _oracle_head(args):
     return t0, time.time()
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def block_tokens(wl) -> int:
+    """Tokens per block the forward kernel runs for this workload: the library serves a
+    chunk above 32 with 32-token blocks for bf16, and for fp32 at K = 128 (the same
+    function; the block is an internal tiling)."""
+    return min(wl.chunk, 32) if (wl.dtype == "bf16" or wl.K == 128) else wl.chunk
+
+
+def copy_bandwidth_gbs(torch, mib: int = 1024, launches: int = 10) -> float:
+    """Device-to-device copy bandwidth (read + write bytes per second), the practical
+    ceiling an HBM-bound kernel is compared with besides the 8 TB/s peak."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(launches):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    secs = a.elapsed_time(b) * 1e-3 / launches
+    del src, dst
+    return 2 * n / secs / 1e9
+
+
 def cpu_baseline(wl, n_heads: int, workers: int, scalar_gate: bool = False) -> dict:
     """The f64 oracle (gate + token recurrence) on n_heads whole heads, one per process:
     head-tokens per second of wall time from the first head's start to the last head's
@@ -101,6 +138,7 @@ def cpu_baseline(wl, n_heads: int, workers: int, scalar_gate: bool = False) -> d
     wall = max(e for _, e in spans) - min(s for s, _ in spans)
     cpu = sum(e - s for s, e in spans)
     return {"value": n_heads * wl.T / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cores": os.cpu_count(),
             "sample": "%d of %d heads at full T=%d (f64 numpy token recurrence, one head per process; "
                       "%.1f s wall, %.1f s of CPU work)" % (n_heads, wl.B * wl.H, wl.T, wall, cpu)}
 
@@ -172,6 +210,36 @@ def decode_bench(B, steps, warmup, H=32, K=128, V=128):
                       "bytes_per_step": nbytes, "steps": steps,
                       "config": {"B": B, "H": H, "K": K, "V": V, "activations": "bf16", "state": "f32"},
                       "note": "HIP events around the launches; includes launch gaps when the host is slower"}))
+
+
+def gate_bench(steps, warmup):
+    """The standalone gate (kda_gate: g and alpha, fp32) over the long workload's gate
+    input (4 x 32 heads x 16384 tokens x 128 channels, bf16): 10 bytes per element."""
+    import torch
+    import gated_delta_rule_47_amd as kda
+    dev = torch.device("cuda:0")
+    B, H, T, K = 4, 32, 16384, 128
+    gen = torch.Generator(device=dev).manual_seed(11)
+    z = torch.randn(B, H, T, K, device=dev, generator=gen).to(torch.bfloat16)
+    A_log = torch.linspace(-2.0, 1.0, H, device=dev)
+    dt_bias = 0.5 * torch.randn(H, K, device=dev, generator=gen)
+    for _ in range(warmup):
+        kda.gate(z, A_log, dt_bias)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        kda.gate(z, A_log, dt_bias)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    nbytes = B * H * T * K * (2 + 4 + 4)
+    print(json.dumps({"metric": "gate bandwidth (kda_gate, g and alpha)", "value": round(nbytes / us / 1e3, 1),
+                      "unit": "GB/s", "frac_of_8TBps": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                      "us_per_call": round(us, 2), "bytes_per_call": nbytes, "steps": steps,
+                      "config": {"B": B, "H": H, "T": T, "K": K, "z": "bf16", "outputs": "f32 g, alpha"},
+                      "note": "HIP events around the calls (each allocates its two outputs through torch's "
+                              "caching allocator)"}))
 
 
 FP32_PEAK_TFLOPS = 157.3      # MI355X dense fp32 (matrix), published
@@ -265,6 +333,8 @@ def main():
     ap.add_argument("--scalar-gate", action="store_true",
                     help="time kda_chunk_fwd_scalar instead (one gate input per head-token: channel 0 of the "
                          "workload's z, bias channel 0 of its dt_bias); a separate metric line")
+    ap.add_argument("--gate", action="store_true",
+                    help="instead of the benchmark, time the standalone gate (kda_gate) on the long workload's z")
     ap.add_argument("--adjoint", action="store_true",
                     help="instead of the benchmark, time kda_chunk_bwd on the adjoint workload (fp32)")
     args = ap.parse_args()
@@ -280,6 +350,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": n, "launches": args.steps}))
+        return
+    if args.gate:
+        gate_bench(args.steps, min(args.warmup, 10))
         return
     if args.adjoint:
         adjoint_bench(args.steps, min(args.warmup, 5))
@@ -345,6 +418,9 @@ def main():
     if workspace is not None and kda.chunk_fwd_status(workspace) != 0:
         raise SystemExit("the paired forward reported a failed exchange")
 
+    # the copy ceiling, measured after the timed region on the same (warm) GPU
+    copy_gbs = copy_bandwidth_gbs(torch)
+
     ms_per_step = wall * 1e3 / args.steps
     avg_kernel_ms = float(np.mean(kern_ms))
     tokens = wl.B * wl.H * wl.T
@@ -361,6 +437,7 @@ def main():
             traffic = None
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "copy_GBps": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4),
             "kernel": kernel_label(wl, args.scalar_gate, paired=workspace is not None),
             "algorithmic_bytes_per_launch": nbytes,
             "avg_kernel_ms": round(avg_kernel_ms, 4), "min_kernel_ms": round(float(np.min(kern_ms)), 4)}
@@ -376,7 +453,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "K": wl.K, "V": wl.V, "chunk": wl.chunk,
-                   "activations": wl.dtype, "state": "f32", "global_batch": wl.B, "seq_len": wl.T,
+                   "block": block_tokens(wl), "activations": wl.dtype, "state": "f32", "global_batch": wl.B, "seq_len": wl.T,
                    "parallelism": "single-gpu"},
         "roofline": roof, "cpu_baseline": cpu,
     }

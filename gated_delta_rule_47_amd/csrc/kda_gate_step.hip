@@ -1,9 +1,10 @@
 // Standalone gate kernel and the single-token decode step.
 //
 // Gate: the released KDA decay form g = -exp(clamp(A_log)) * softplus(z + dt_bias),
-// alpha = exp(g) (kdafix page, "Fix 1 -- decay form").  Elementwise, HBM-bound:
-// each thread handles one element per grid-stride step; consecutive lanes touch
-// consecutive addresses.
+// alpha = exp(g) (kdafix page, "Fix 1 -- decay form").  Elementwise, HBM-bound: one
+// workgroup per (batch, head, tile of kGateTile tokens), so the head's multiplier and
+// each thread's channel bias are read once; consecutive lanes touch consecutive
+// addresses of a token row.
 //
 // Decode step: one token of the gated delta rule per (batch, head), the state read
 // and written in place.  The state dominates the traffic (2*K*V*4 bytes per head),
@@ -20,19 +21,32 @@
 
 namespace kda {
 
+constexpr int kGateTile = 64;
+
+// Thread tid covers channel cb + tid % KC of every (256 / KC)-th token row of the tile,
+// for each pass cb of up to 256 channels.
 template <typename Tin>
 __global__ void __launch_bounds__(256) gate_kernel(const Tin* __restrict__ z, const float* __restrict__ A_log,
                                                    const float* __restrict__ dt_bias, float* __restrict__ g_out,
-                                                   float* __restrict__ alpha_out, int H, int T, int K, long long n) {
-  const long long stride = (long long)gridDim.x * blockDim.x;
-  for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += stride) {
-    const int c = (int)(idx % K);
-    const int h = (int)((idx / K / T) % H);
-    const float mult = gate_multiplier(A_log[h]);
-    const float x = to_f<Tin>(z[idx]) + (dt_bias ? dt_bias[h * K + c] : 0.0f);
-    const float g = -mult * softplus_f(x, true);
-    g_out[idx] = g;
-    if (alpha_out) alpha_out[idx] = fast_exp2(g * kLog2e);
+                                                   float* __restrict__ alpha_out, int H, int T, int K, int ntile) {
+  const int wg = blockIdx.x;
+  const int bh = wg / ntile, tile = wg - bh * ntile;
+  const int h = bh % H;
+  const int t0 = tile * kGateTile, t1 = min(T, t0 + kGateTile);
+  const float mult = gate_multiplier(A_log[h]);
+  const int tid = threadIdx.x;
+  for (int cb = 0; cb < K; cb += 256) {
+    const int KC = min(K - cb, 256);           // channels of this pass
+    const int rpp = 256 / KC;                  // token rows per pass
+    const int r = tid / KC, c = cb + tid % KC;
+    if (r >= rpp) continue;
+    const float db = dt_bias ? dt_bias[h * K + c] : 0.0f;
+    for (int t = t0 + r; t < t1; t += rpp) {
+      const size_t idx = ((size_t)bh * T + t) * K + c;
+      const float g = -mult * softplus_f(to_f<Tin>(z[idx]) + db, true);
+      g_out[idx] = g;
+      if (alpha_out) alpha_out[idx] = fast_exp2(g * kLog2e);
+    }
   }
 }
 
@@ -192,12 +206,12 @@ __global__ void __launch_bounds__(256) step_kernel(const Tin* __restrict__ q, co
 template <typename Tin>
 hipError_t launch_gate(const void* z, const float* A_log, const float* dt_bias, float* g, float* alpha,
                        int B, int H, int T, int K, hipStream_t s) {
-  const long long n = (long long)B * H * T * K;
-  if (n == 0) return hipSuccess;
-  long long blocks = (n + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
+  const int ntile = (T + kGateTile - 1) / kGateTile;
+  const long long blocks = (long long)B * H * ntile;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gate_kernel<Tin>, dim3((unsigned)blocks), dim3(256), 0, s, (const Tin*)z, A_log, dt_bias, g,
-                     alpha, H, T, K, n);
+                     alpha, H, T, K, ntile);
   return hipGetLastError();
 }
 

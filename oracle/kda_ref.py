@@ -20,6 +20,7 @@ What the method computes (per batch b and head h, all in float64):
   read scale  q_hat = scale * q, default scale = K**-0.5                    [fix, Fix 2]
   scalar decay  one pre-activation per token and one bias per head: the same gate,
               the same alpha on every key channel (gate_scalar, recurrent_scalar)
+  output norm y = o / sqrt(mean_v(o^2) + eps) * weight_h (rmsnorm; reading R20)
   recurrence  S' = diag(alpha_t) S_{t-1}
               S_t = S' + beta_t k_t (v_t - S'^T k_t)^T
               o_t = S_t^T q_hat_t
@@ -356,6 +357,22 @@ def fd_directional(fn, x, direction, h=1e-6):
     x = np.asarray(x, dtype=np.float64)
     d = np.asarray(direction, dtype=np.float64)
     return (fn(x + h * d) - fn(x - h * d)) / (2.0 * h)
+
+
+# ============================================================================ output norm
+def rmsnorm(o, weight=None, eps=1e-6):
+    """The RMSNorm that follows the read (reading R20: over each head's V outputs of a
+    token, one weight row per head, no gate):
+        y[b, h, t, :] = o[b, h, t, :] / sqrt(mean_v o[b, h, t, v]^2 + eps) * weight[h, :]
+    o (B, H, T, V); weight (H, V) or None (all ones); eps >= 0.  [fix, Fix 2: the module
+    normalises the read right after it, so a constant factor on o, such as the read
+    scale, changes y only through eps, by O(eps / mean(o^2)).]"""
+    o = np.asarray(o, dtype=np.float64)
+    ms = np.mean(o * o, axis=-1, keepdims=True)
+    y = o / np.sqrt(ms + eps)
+    if weight is not None:
+        y = y * np.asarray(weight, dtype=np.float64)[None, :, None, :]
+    return y
 
 
 # ============================================================================ metrics

@@ -162,3 +162,33 @@ def test_gate_adjoint_mutants_fail_pins(monkeypatch, mutant):
         except AssertionError:
             failed += 1
     assert failed >= 1
+
+
+# ----------------------------------------------------------------------------- output RMSNorm mutants
+def _rms_sum_not_mean(o, weight=None, eps=1e-6):
+    o = np.asarray(o, dtype=np.float64)
+    y = o / np.sqrt(np.sum(o * o, axis=-1, keepdims=True) + eps)
+    return y if weight is None else y * np.asarray(weight)[None, :, None, :]
+
+
+def _rms_over_tokens(o, weight=None, eps=1e-6):
+    o = np.asarray(o, dtype=np.float64)
+    y = o / np.sqrt(np.mean(o * o, axis=-2, keepdims=True) + eps)
+    return y if weight is None else y * np.asarray(weight)[None, :, None, :]
+
+
+def _rms_eps_outside(o, weight=None, eps=1e-6):
+    o = np.asarray(o, dtype=np.float64)
+    y = o / (np.sqrt(np.mean(o * o, axis=-1, keepdims=True)) + eps)
+    return y if weight is None else y * np.asarray(weight)[None, :, None, :]
+
+
+@pytest.mark.parametrize("mutant", [_rms_sum_not_mean, _rms_over_tokens, _rms_eps_outside])
+def test_rmsnorm_mutants_fail_the_hand_rows(monkeypatch, mutant):
+    ex = GOLD["rmsnorm_rows"]
+    monkeypatch.setattr(R, "rmsnorm", mutant)
+    bad = 0
+    for case in ex["cases"]:
+        y = R.rmsnorm(np.array(ex["o"]), np.array(ex["weight"]), eps=case["eps"])
+        bad += not np.allclose(y, np.array(case["y"]), rtol=0, atol=ex["tol"])
+    assert bad >= 1

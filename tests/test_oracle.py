@@ -274,3 +274,50 @@ def test_rel_err_definition():
     ref = np.array([1.0, -4.0, 2.0])
     assert R.rel_err(ref + np.array([0.0, 0.4, 0.0]), ref) == pytest.approx(0.1)
     assert R.rel_err(np.zeros(3), np.zeros(3)) == 0.0
+
+
+# ----------------------------------------------------------------------------- output RMSNorm (reading R20)
+def test_rmsnorm_hand_rows():
+    """Two hand-worked rows, with and without eps (tests/golden, 'rmsnorm_rows'): the mean
+    runs over the V outputs of one token (not over tokens, not a sum), and the weight row
+    multiplies after the division."""
+    ex = GOLD["rmsnorm_rows"]
+    o = np.array(ex["o"])
+    w = np.array(ex["weight"])
+    for case in ex["cases"]:
+        y = R.rmsnorm(o, w, eps=case["eps"])
+        assert np.allclose(y, np.array(case["y"]), rtol=0, atol=ex["tol"]), case["derivation"]
+
+
+def test_rmsnorm_absorbs_the_read_scale_to_eps_over_mean_square():
+    """kdafix page, 'Fix 2 -- read scale': the norm after the read absorbs a constant
+    factor on o up to O(eps / mean(o^2)).  For o and c o the rows differ by the factor
+    sqrt((m + eps) / (m + eps / c^2)) (m = mean(o^2)), which lies in (1, 1 + eps / (2m)];
+    with eps = 0 the norm is exactly invariant.  c = 8**0.5 is the page's K = 8 ratio."""
+    rng = np.random.default_rng(3)
+    o = rng.standard_normal((2, 3, 5, 16)) + 0.5
+    w = rng.uniform(0.5, 2.0, (3, 16))
+    c = GOLD["read_scale_ratio_K8"]["ratio"]
+    eps = 1e-5
+    y1, yc = R.rmsnorm(o, w, eps), R.rmsnorm(c * o, w, eps)
+    m = np.mean(o * o, axis=-1, keepdims=True)
+    ratio = yc / y1
+    assert np.allclose(ratio, np.sqrt((m + eps) / (m + eps / c ** 2)), rtol=1e-13, atol=0)
+    assert np.all(ratio > 1.0) and np.all(ratio - 1.0 <= eps / (2 * m) * (1 + 1e-9))
+    assert np.max(np.abs(yc - y1)) / np.max(np.abs(y1)) < 1e-4        # "~1e-5" at mean(o^2) ~ 1
+    assert np.allclose(R.rmsnorm(c * o, w, 0.0), R.rmsnorm(o, w, 0.0), rtol=1e-14, atol=0)
+
+
+def test_rmsnorm_unit_mean_square_and_per_head_weight():
+    """With eps = 0 and no weight every row has mean square 1; a weight row acts on its
+    own head only, column by column."""
+    rng = np.random.default_rng(4)
+    o = rng.standard_normal((2, 3, 7, 8))
+    y = R.rmsnorm(o, None, 0.0)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, rtol=1e-14, atol=0)
+    w = np.ones((3, 8))
+    w[1, 2] = 3.0
+    yw = R.rmsnorm(o, w, 0.0)
+    assert np.array_equal(yw[:, [0, 2]], y[:, [0, 2]])
+    assert np.allclose(yw[:, 1, :, 2], 3.0 * y[:, 1, :, 2], rtol=1e-15, atol=0)
+    assert np.array_equal(np.delete(yw[:, 1], 2, axis=-1), np.delete(y[:, 1], 2, axis=-1))

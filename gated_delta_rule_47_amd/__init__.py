@@ -18,7 +18,8 @@ import torch
 from . import _lib
 
 __all__ = ["KdaError", "read_scale", "gate", "chunk_fwd", "chunk_fwd_scalar", "chunk_fwd_workspace_bytes",
-           "chunk_fwd_status", "set_exchange_timeout_us", "recurrent_step", "recurrent_step_scalar", "chunk_bwd",
+           "chunk_fwd_status", "set_exchange_timeout_us", "chunk_fwd_norm",
+           "chunk_fwd_norm_workspace_bytes", "recurrent_step", "recurrent_step_scalar", "chunk_bwd",
            "chunk_bwd_workspace_bytes", "gate_bwd", "gate_bwd_workspace_bytes", "gate_bwd_noalloc",
            "GATE_BWD_SCRATCH_BYTES", "counters", "status_string",
            "library_path"]
@@ -195,6 +196,48 @@ def _chunk_fwd(fn, q, k, v, z, A_log, dt_bias, beta, state_in, scale, chunk, out
     _call(fn, _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(dt_bias), _ptr(beta),
           _ptr(state_in), float(scale), int(chunk), _ptr(o), _ptr(state_out), _ptr(workspace), wbytes,
           B, H, T, K, V, _dtype_code(q), _stream(q.device))
+    return o, state_out
+
+
+def chunk_fwd_norm_workspace_bytes(B, H, T, K, V, dtype=torch.bfloat16) -> int:
+    code = _lib.KDA_BF16 if dtype == torch.bfloat16 else _lib.KDA_F32
+    return int(_lib.load().kda_chunk_fwd_norm_workspace_bytes(B, H, T, K, V, code))
+
+
+def chunk_fwd_norm(q, k, v, z, A_log, dt_bias, beta, state_in=None, norm_weight=None, eps=1e-6, scale=None,
+                   chunk=64, output_state=True, out=None, state_out=None, workspace="auto"):
+    """chunk_fwd with the output RMSNorm fused into its output stage (bf16 only): o holds
+    r / sqrt(mean_v r^2 + eps) * norm_weight[h] for the read r.  norm_weight (H, V) float32
+    or None (ones).  workspace: "auto" allocates (zero-filled) what
+    chunk_fwd_norm_workspace_bytes() asks for (nonzero when V > 64), or a uint8 CUDA tensor
+    of at least that size, zero-filled before its first use and used for this call only."""
+    B, H, T, K, V = _check_acts(q, k, v, z, beta)
+    _check_f32("A_log", A_log, (H,))
+    _check_f32("dt_bias", dt_bias, (H, K))
+    _check_f32("state_in", state_in, (B, H, K, V))
+    _check_f32("norm_weight", norm_weight, (H, V))
+    _check_out("out", out, (B, H, T, V), q.dtype, q.device)
+    _check_out("state_out", state_out, (B, H, K, V), torch.float32, q.device)
+    if scale is None:
+        scale = read_scale(K)
+    o = out if out is not None else torch.empty((B, H, T, V), dtype=q.dtype, device=q.device)
+    if output_state and state_out is None:
+        state_out = torch.empty((B, H, K, V), dtype=torch.float32, device=q.device)
+    if not output_state:
+        state_out = None
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a tensor")
+        need = chunk_fwd_norm_workspace_bytes(B, H, T, K, V, q.dtype)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device) if need else None
+    wbytes = 0
+    if workspace is not None:
+        if workspace.device != q.device:
+            raise ValueError("workspace is on %s, expected %s" % (workspace.device, q.device))
+        wbytes = workspace.numel() * workspace.element_size()
+    _call("kda_chunk_fwd_norm", _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(dt_bias), _ptr(beta),
+          _ptr(state_in), float(scale), int(chunk), _ptr(norm_weight), float(eps), _ptr(o), _ptr(state_out),
+          _ptr(workspace), wbytes, B, H, T, K, V, _dtype_code(q), _stream(q.device))
     return o, state_out
 
 

@@ -14,7 +14,7 @@ COUNTER_NAMES = ("gate", "chunk_fwd", "recurrent_step", "chunk_bwd", "rejected",
 EXPORTED = ("kda_read_scale", "kda_gate", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_scalar",
             "kda_chunk_fwd_status", "kda_set_exchange_timeout_us", "kda_recurrent_step",
             "kda_recurrent_step_scalar",
-            "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_gate_bwd_workspace_bytes", "kda_gate_bwd", "kda_gate_bwd_noalloc",
+            "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_gate_bwd_workspace_bytes", "kda_gate_bwd", "kda_gate_bwd_noalloc", "kda_chunk_fwd_norm_workspace_bytes", "kda_chunk_fwd_norm",
             "kda_status_string", "kda_get_counters")
 
 _lib = None
@@ -28,6 +28,9 @@ _PROTOS = {
     "kda_read_scale": (_f, [_i]),
     "kda_gate": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "kda_chunk_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "kda_chunk_fwd_norm_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "kda_chunk_fwd_norm": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p, _f, _p, _p, _p, _sz, _i, _i, _i, _i, _i, _i,
+                                _p]),
     "kda_chunk_fwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p, _p, _p, _sz, _i, _i, _i, _i, _i, _i, _p]),
     "kda_chunk_fwd_scalar": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p, _p, _p, _sz, _i, _i, _i, _i, _i, _i,
                                   _p]),

@@ -169,6 +169,10 @@ static int chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     return reject(KDA_ERR_ALIAS);
   if (state_out && state_in && state_out != state_in && overlap(state_out, ns, state_in, ns))
     return reject(KDA_ERR_ALIAS);
+  const size_t na = (size_t)H * 4, ndb = (size_t)H * (zc ? K : 1) * 4;
+  if (overlap(o, nv, A_log, na) || overlap(o, nv, dt_bias, ndb) || overlap(state_out, ns, A_log, na) ||
+      overlap(state_out, ns, dt_bias, ndb))
+    return reject(KDA_ERR_ALIAS);
   FwdPlan plan;
   if (!fwd_plan(dtype == KDA_BF16, K, V, chunk, &plan)) return reject(KDA_ERR_SHAPE);
   // paired path: needs the workspace (without one, each value tile recomputes the
@@ -211,6 +215,69 @@ static int chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
   } else {
     e = launch_fwd(dtype == KDA_BF16, plan, q, k, v, z, A_log, dt_bias, beta, state_in, scale, o, state_out, B, H, T,
                    K, V, zc, s);
+  }
+  if (e != hipSuccess) return reject(KDA_ERR_HIP);
+  g_counters[KDA_COUNTER_CHUNK_FWD].fetch_add(1, std::memory_order_relaxed);
+  return KDA_OK;
+}
+
+// kda_chunk_fwd_norm: the checks of kda_chunk_fwd (bf16 only), the weight row and eps,
+// the workspace when the two value tiles of a head exchange sums; then the launches.
+static int chunk_fwd_norm_impl(const void* q, const void* k, const void* v, const void* z, const float* A_log,
+                               const float* dt_bias, const void* beta, const float* state_in, float scale,
+                               int chunk, const float* norm_w, float eps, void* o, float* state_out,
+                               void* workspace, size_t workspace_bytes, int B, int H, int T, int K, int V, int dtype,
+                               void* stream) {
+  if (!A_log || (T != 0 && (!q || !k || !v || !z || !beta || !o))) return reject(KDA_ERR_NULL);
+  if (dtype != KDA_BF16) return reject(KDA_ERR_DTYPE);
+  if (B < 1 || H < 1 || T < 0 || !valid_dim(K) || !valid_dim(V)) return reject(KDA_ERR_SHAPE);
+  if (!(eps >= 0.0f && eps <= 3.0e38f)) return reject(KDA_ERR_SHAPE);
+  if (!valid_chunk(chunk)) return reject(KDA_ERR_CHUNK);
+  if ((size_t)(T + 64) * (size_t)(K > V ? K : V) * 2 > 0x7fffffffu) return reject(KDA_ERR_SHAPE);
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)z) & 3) return reject(KDA_ERR_ALIGN);
+  if ((uintptr_t)o & 7) return reject(KDA_ERR_ALIGN);
+  const size_t nk = (size_t)B * H * T * K * 2, nv = (size_t)B * H * T * V * 2, nb = (size_t)B * H * T * 2;
+  const size_t ns = (size_t)B * H * K * V * 4, na = (size_t)H * 4, ndb = (size_t)H * K * 4, nw = (size_t)H * V * 4;
+  struct Buf { const void* p; size_t n; };
+  const Buf ins[] = {{q, nk}, {k, nk}, {v, nv}, {z, nk}, {beta, nb}, {A_log, na}, {dt_bias, ndb}, {norm_w, nw}};
+  for (const Buf& b : ins)
+    if (overlap(o, nv, b.p, b.n) || overlap(state_out, ns, b.p, b.n)) return reject(KDA_ERR_ALIAS);
+  if (overlap(o, nv, state_in, ns) || overlap(o, nv, state_out, ns)) return reject(KDA_ERR_ALIAS);
+  if (state_out && state_in && state_out != state_in && overlap(state_out, ns, state_in, ns))
+    return reject(KDA_ERR_ALIAS);
+  const size_t need = T > 0 ? norm_workspace_bytes(B, H, T, V) : 0;
+  if (need) {
+    if (!workspace || workspace_bytes < need) return reject(KDA_ERR_WORKSPACE);
+    if ((uintptr_t)workspace & 255) return reject(KDA_ERR_ALIGN);
+    const Buf all[] = {{q, nk}, {k, nk}, {v, nv}, {z, nk}, {beta, nb}, {state_in, ns}, {o, nv}, {state_out, ns},
+                       {A_log, na}, {dt_bias, ndb}, {norm_w, nw}};
+    for (const Buf& b : all)
+      if (overlap(workspace, need, b.p, b.n)) return reject(KDA_ERR_ALIAS);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (T == 0) {
+    if (state_out && state_out != state_in) {
+      const long long n = (long long)B * H * K * V;
+      hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, state_in, state_out,
+                         n);
+      e = hipGetLastError();
+    }
+  } else {
+    const unsigned long long spin = g_spin_ticks.load(std::memory_order_relaxed);
+    switch (K < 32 ? 32 : K) {
+      case 32:
+        e = launch_chunk_fwd_norm_kd<32>(q, k, v, z, A_log, dt_bias, beta, state_in, scale, norm_w, eps, o, state_out,
+                                         B, H, T, K, V, workspace, spin, s);
+        break;
+      case 64:
+        e = launch_chunk_fwd_norm_kd<64>(q, k, v, z, A_log, dt_bias, beta, state_in, scale, norm_w, eps, o, state_out,
+                                         B, H, T, K, V, workspace, spin, s);
+        break;
+      default:
+        e = launch_chunk_fwd_norm_kd<128>(q, k, v, z, A_log, dt_bias, beta, state_in, scale, norm_w, eps, o,
+                                          state_out, B, H, T, K, V, workspace, spin, s);
+    }
   }
   if (e != hipSuccess) return reject(KDA_ERR_HIP);
   g_counters[KDA_COUNTER_CHUNK_FWD].fetch_add(1, std::memory_order_relaxed);
@@ -262,6 +329,19 @@ int kda_chunk_fwd_scalar(const void* q, const void* k, const void* v, const void
                          int K, int V, int dtype, void* stream) {
   return chunk_fwd_impl(q, k, v, a, A_log, dt_bias, beta, state_in, scale, chunk, o, state_out, workspace,
                         workspace_bytes, B, H, T, K, V, dtype, stream, 0);
+}
+
+size_t kda_chunk_fwd_norm_workspace_bytes(int B, int H, int T, int K, int V, int dtype) {
+  if (B < 1 || H < 1 || T < 1 || !valid_dim(K) || !valid_dim(V) || dtype != KDA_BF16) return 0;
+  return norm_workspace_bytes(B, H, T, V);
+}
+
+int kda_chunk_fwd_norm(const void* q, const void* k, const void* v, const void* z, const float* A_log,
+                       const float* dt_bias, const void* beta, const float* state_in, float scale, int chunk,
+                       const float* norm_weight, float eps, void* o, float* state_out, void* workspace,
+                       size_t workspace_bytes, int B, int H, int T, int K, int V, int dtype, void* stream) {
+  return chunk_fwd_norm_impl(q, k, v, z, A_log, dt_bias, beta, state_in, scale, chunk, norm_weight, eps, o, state_out,
+                             workspace, workspace_bytes, B, H, T, K, V, dtype, stream);
 }
 
 int kda_chunk_fwd_status(void* workspace, void* stream) {

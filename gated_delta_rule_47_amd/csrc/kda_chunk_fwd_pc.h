@@ -123,6 +123,32 @@ struct PcCfg {
                 "16-byte alignment");
 };
 
+// LDS of the fused output norm, after the walk's own regions.  The output of a block is
+// held for D steps (until the other value tile's sums of squares of its tokens have
+// arrived): per block slot, each V wave's 32 x 16 bf16 output tile in its lanes' order
+// (16 bytes per lane) and, per token, 16 partial sums of squares (one per V wave and
+// lane group of 4 columns, contiguous), plus the weight row of the tile.
+template <int KD, int VT, int C>
+struct PnCfg {
+  using Cfg = PcCfg<KD, VT, C>;
+  static constexpr int D = 3, NH = 4;                 // steps a block is held; slots (> D)
+  static constexpr int HELD_SLOT = Cfg::NV * 1024;
+  static constexpr int NPART = Cfg::NV * 4;           // partial sums per token
+  static constexpr int PSUM_SLOT = 32 * NPART * 4;
+  static constexpr int OFF_HELD = round_up(Cfg::TOTAL, 16);
+  static constexpr int OFF_PSUM = OFF_HELD + NH * HELD_SLOT;
+  static constexpr int OFF_NW = OFF_PSUM + NH * PSUM_SLOT;
+  static constexpr int TOTAL = OFF_NW + Cfg::VD * 4;
+  static_assert((NH & (NH - 1)) == 0 && NH > D, "norm slots");
+};
+
+// Workspace of the fused norm when a head has two value tiles: a header (word 0: status,
+// word 1: call epoch), then per (head, tile, block, token) one 8-byte word {sum of
+// squares of the tile's outputs (fp32 bits), epoch}.
+constexpr int PN_HEADER = 256;
+constexpr int PN_MAX_HEADS = 128;               // heads per launch: both tiles resident
+constexpr unsigned PN_STATUS_TIMEOUT = 1;       // a wait for the other tile's sums ran out
+
 // Storage position of contraction index x inside its 32-wide slice: the indices
 // {4g..4g+3, 16+4g..16+4g+3} that lane group g supplies to an MFMA are made contiguous.
 __device__ __forceinline__ constexpr int perm32(int x) {
@@ -171,6 +197,14 @@ __device__ __forceinline__ void store4_bf16(bf16_t* dst, float a, float b, float
 }
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 8 bytes at buffer offset `off`, device scope (sc1): misses the CU's vector cache and
+// reads L2, so another workgroup's stores on the same XCD are seen.
+__device__ __forceinline__ u32x2 load_b64_dev(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 16);
+}
+
 
 // Keep the compiler from moving instructions across this point: used to issue a
 // batch of LDS operand loads before the MFMAs that consume them.
@@ -237,7 +271,7 @@ __device__ __attribute__((noinline)) void token_block(float* stl, const bf16_t* 
                                                      const bf16_t* v, const bf16_t* z, const bf16_t* beta,
                                                      const float* dt_bias, bf16_t* o, int T, int K, int V, int v0,
                                                      int vcols, int t0, int nval, float mult2, float scale,
-                                                     int lane, int col) {
+                                                     int lane, int col, bf16_t* held, float* psum) {
   constexpr unsigned kOOB = 0xFFFFFFF0u;
   const int g = lane >> 4;
   const __amdgpu_buffer_rsrc_t tz = make_rsrc(z, (unsigned)(T * (SG ? 1 : K) * 2));
@@ -296,25 +330,42 @@ __device__ __attribute__((noinline)) void token_block(float* stl, const bf16_t* 
     }
     op += __shfl_xor(op, 16);
     op += __shfl_xor(op, 32);
-    if (g == 0 && col < vcols)
+    if (held) {
+      // fused norm: into the held tile, in the lane order of the MFMA path (token i of
+      // the block at lane (i % 16) + 16 * (column % 16 / 4), half i / 16, element column % 4),
+      // and the token's sum of squares over this wave's 16 columns
+      if (g == 0) held[((i & 15) + 16 * ((col & 15) >> 2)) * 8 + (i >> 4) * 4 + (col & 3)] = f2bf(op);
+      float sq = col < vcols ? op * op : 0.0f;
+      sq += __shfl_xor(sq, 1);
+      sq += __shfl_xor(sq, 2);
+      sq += __shfl_xor(sq, 4);
+      sq += __shfl_xor(sq, 8);
+      if (lane < 4) psum[i * 16 + lane] = lane == 0 ? sq : 0.0f;   // this wave's 4 partials
+    } else if (g == 0 && col < vcols) {
       __builtin_amdgcn_raw_buffer_store_b16(f2bf(op), to, (unsigned)((tok * V + v0 + col) * 2), 0, 0);
+    }
   }
 }
 
-template <int KD, int VT, int C, bool SG>
+template <int KD, int VT, int C, bool SG, bool NORM = false>
 __global__ void __launch_bounds__(1024)
 chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                     const bf16_t* __restrict__ z, const float* __restrict__ A_log,
                     const float* __restrict__ dt_bias, const bf16_t* __restrict__ beta,
                     const float* state_in, float scale, bf16_t* __restrict__ o, float* state_out, int H, int T,
-                    int K, int V, int n_vtiles, int total_wg, float thresh) {
+                    int K, int V, int n_vtiles, int total_wg, float thresh, const float* __restrict__ norm_w,
+                    float eps, unsigned char* __restrict__ work, unsigned long long spin_ticks, int head0,
+                    int nlaunch) {
   using Cfg = PcCfg<KD, VT, C>;
+  using Pn = PnCfg<KD, VT, C>;
+  constexpr int SMEM = NORM ? Pn::TOTAL : Cfg::TOTAL;
+  static_assert(!NORM || (C == 32 && Pn::TOTAL <= 160 * 1024), "norm: 32-token blocks, LDS budget");
   constexpr int CD = Cfg::CD, NB = Cfg::NB, NNT = Cfg::NNT, NMT = Cfg::NMT;
   constexpr int LD_TK = Cfg::LD_TK, LD_CT = Cfg::LD_CT, LD_A = Cfg::LD_A;
   constexpr int NS = KD / 32;                         // 32-deep channel slices
   constexpr int NTHR = Cfg::NWAVES * 64;
 
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
   float* sA = reinterpret_cast<float*>(smem + Cfg::OFF_A);
   int* sFlag = reinterpret_cast<int*>(smem + Cfg::OFF_FLAG);   // [block % 3][E wave]
   // Buffer offsets of block b, passed through an empty asm so that the compiler keeps them
@@ -350,16 +401,34 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   const int l16 = lane & 15;
   const int g = lane >> 4;
 
-  int p = blockIdx.x;
-  if ((total_wg & 7) == 0) p = (blockIdx.x & 7) * (total_wg >> 3) + (blockIdx.x >> 3);
-  const int bh = p / n_vtiles;
-  const int v0 = (p % n_vtiles) * VT;
+  int bh, v0, role = 0;
+  bool paired = false;                         // fused norm over two value tiles
+  if constexpr (NORM) {
+    // the two tiles of head head0 + 8g + j are workgroups 16g + j and 16g + j + 8, which
+    // the hardware places on one XCD (workgroup i runs on XCD i % 8): they share its L2
+    if (n_vtiles == 2) {
+      const int pr = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
+      if (pr >= nlaunch) return;
+      role = (blockIdx.x >> 3) & 1;
+      bh = head0 + pr;
+      paired = true;
+    } else {
+      if ((int)blockIdx.x >= nlaunch) return;
+      bh = head0 + blockIdx.x;
+    }
+    v0 = role * VT;
+  } else {
+    int p = blockIdx.x;
+    if ((total_wg & 7) == 0) p = (blockIdx.x & 7) * (total_wg >> 3) + (blockIdx.x >> 3);
+    bh = p / n_vtiles;
+    v0 = (p % n_vtiles) * VT;
+  }
   const int h = bh % H;
   const int vcols = min(VT, V - v0);
   const size_t tb = (size_t)bh * T;
   const int nck = (T + C - 1) / C;
 
-  for (int i = tid; i < Cfg::TOTAL / 16; i += NTHR) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i < SMEM / 16; i += NTHR) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
 
   const float gmul = gate_multiplier(A_log[h]);
   const float mult2 = gmul * kLog2e;
@@ -766,6 +835,20 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           if (row < K && col < vcols) sacc[mt][r] = state_in[((size_t)bh * K + row) * V + v0 + col];
         }
     }
+    // Fused norm: this wave's 16 weights into LDS (1 without a weight row, 0 past the
+    // tile's columns), the call's epoch from the workspace header.
+    float* const nwl = reinterpret_cast<float*>(smem + Pn::OFF_NW);
+    float* const psum = reinterpret_cast<float*>(smem + Pn::OFF_PSUM);
+    unsigned epoch = 0;
+    bool dead = false;                         // a wait for the other tile gave up
+    if constexpr (NORM) {
+      if (vact && lane < 16) {
+        const int c = 16 * vw + lane;
+        nwl[c] = c < vcols ? (norm_w ? norm_w[(size_t)h * V + v0 + c] : 1.0f) : 0.0f;
+      }
+      if (paired)
+        epoch = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(work, 8u), 4, 0, 0));
+    }
     // Complete the state loads here: inside the walk the wave's only vector-memory
     // operations are its output stores, which must never hold up the next step.
     wait_vm();
@@ -776,6 +859,87 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     // output rows of this head through a buffer resource: 32-bit offsets, no 64-bit
     // address arithmetic per store
     const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(o + tb * V, o ? (unsigned)(T * V * 2) : 0u);
+
+    // Fused norm.  Words of value tile `tile` of this head: one per (block, token).
+    auto ring_rsrc = [&](int tile) __attribute__((always_inline)) {
+      const size_t row = (size_t)nck * 256;
+      return make_rsrc(work + PN_HEADER + ((size_t)bh * 2 + tile) * row, (unsigned)row);
+    };
+    // Wave 0 publishes this tile's per-token sums of squares of block b (the V waves wrote
+    // their partial sums during step b): one 8-byte store per token, sum and epoch together.
+    auto norm_export = [&](int b) __attribute__((always_inline)) {
+      const float* ps = psum + (b & (Pn::NH - 1)) * (32 * Pn::NPART);
+      if (lane < 32) {
+        float t = 0.0f;
+#pragma unroll
+        for (int w = 0; w < Pn::NPART; w += 4) {
+          const floatx4 x = *reinterpret_cast<const floatx4*>(ps + lane * Pn::NPART + w);
+          t += (x[0] + x[1]) + (x[2] + x[3]);
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(t), epoch}, ring_rsrc(role),
+                                              (unsigned)((b * 32 + lane) * 8), 0, 0);
+      }
+    };
+    // y = o / sqrt(mean(o^2) + eps) * w for the held block bn: the sums of this tile from
+    // LDS, those of the other tile from its words (waiting, bounded, until both of the
+    // lane's words carry this call's epoch), then the stores.
+    auto norm_out = [&](int bn) __attribute__((always_inline)) {
+      const int slot = bn & (Pn::NH - 1);
+      const int lg = lane >> 4, ll = lane & 15;
+      const float* ps = psum + slot * (32 * Pn::NPART);
+      float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+      for (int w = 0; w < Pn::NPART; w += 4) {
+        const floatx4 x0 = *reinterpret_cast<const floatx4*>(ps + ll * Pn::NPART + w);
+        const floatx4 x1 = *reinterpret_cast<const floatx4*>(ps + (16 + ll) * Pn::NPART + w);
+        s0 += (x0[0] + x0[1]) + (x0[2] + x0[3]);
+        s1 += (x1[0] + x1[1]) + (x1[2] + x1[3]);
+      }
+      if (paired) {
+        const __amdgpu_buffer_rsrc_t rp = ring_rsrc(1 - role);
+        const unsigned off0 = (unsigned)((bn * 32 + ll) * 8), off1 = off0 + 128;
+        u32x2 a = load_b64_dev(rp, off0), c = load_b64_dev(rp, off1);
+        // (a zero bound gives up at once, whether or not the words are there yet)
+        if (!dead && (spin_ticks == 0 || __ballot(a.y != epoch || c.y != epoch) != 0ull)) {
+          dead = spin_ticks == 0;
+          const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+          while (!dead) {
+            __builtin_amdgcn_s_sleep(1);
+            asm volatile("" ::: "memory");     // the loads below are repeated, not hoisted
+            a = load_b64_dev(rp, off0);
+            c = load_b64_dev(rp, off1);
+            if (__ballot(a.y != epoch || c.y != epoch) == 0ull) break;
+            dead = __builtin_amdgcn_s_memrealtime() - t0 > spin_ticks;
+          }
+          if (dead && lane == 0) __builtin_amdgcn_raw_buffer_store_b32(PN_STATUS_TIMEOUT, make_rsrc(work, 8u), 0, 0, 0);
+        }
+        s0 += __uint_as_float(a.x);
+        s1 += __uint_as_float(c.x);
+      }
+      const float inv_v = 1.0f / (float)V;
+      const float r0 = rsqrtf(fmaf(s0, inv_v, eps)), r1 = rsqrtf(fmaf(s1, inv_v, eps));
+      const u32x4 hv = *reinterpret_cast<const u32x4*>(smem + Pn::OFF_HELD + slot * Pn::HELD_SLOT + vw * 1024 + lane * 16);
+      const floatx4 wv = *reinterpret_cast<const floatx4*>(nwl + 16 * vw + 4 * lg);
+      auto lo = [](uint32_t u) { return __uint_as_float(u << 16); };
+      auto hi = [](uint32_t u) { return __uint_as_float(u & 0xffff0000u); };
+      const u32x2 y0 = {pack_bf16x2(lo(hv.x) * r0 * wv[0], hi(hv.x) * r0 * wv[1]),
+                        pack_bf16x2(lo(hv.y) * r0 * wv[2], hi(hv.y) * r0 * wv[3])};
+      const u32x2 y1 = {pack_bf16x2(lo(hv.z) * r1 * wv[0], hi(hv.z) * r1 * wv[1]),
+                        pack_bf16x2(lo(hv.w) * r1 * wv[2], hi(hv.w) * r1 * wv[3])};
+      const int nvb = min(C, T - bn * C);
+      const int c0 = 16 * vw + 4 * lg;
+      if (c0 < vcols) {
+        if (ll < nvb)
+          __builtin_amdgcn_raw_buffer_store_b64(y0, rs_o, (unsigned)(((bn * C + ll) * V + v0 + c0) * 2), 0, 0);
+        if (16 + ll < nvb)
+          __builtin_amdgcn_raw_buffer_store_b64(y1, rs_o, (unsigned)(((bn * C + 16 + ll) * V + v0 + c0) * 2), 0, 0);
+      }
+    };
+    // at the start of step s: publish block s-1, finish block s-D
+    auto norm_step = [&](int s) __attribute__((always_inline)) {
+      if (paired && vw == 0 && s >= 1) norm_export(s - 1);
+      if (vact && s >= Pn::D) norm_out(s - Pn::D);
+    };
 
     // nf0, nf1: the raw slow flags of block b+1, loaded at the top of the step and only
     // examined after phase C, so that their read never stalls the start of a step
@@ -889,7 +1053,25 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
 #pragma unroll
           for (int m = 0; m < NM; ++m) sacc[hd * NM + m] = fs[m] * mfma_bf16(fk[m], ub, sacc[hd * NM + m]);
         }
-        if (o) {
+        if constexpr (NORM) {
+          // held for the norm: the scaled outputs as bf16, and the per-token sums of
+          // squares over this wave's 16 columns taken before rounding
+          static_assert(!NORM || NB == 2, "norm blocks are 32 tokens");
+          const int slot = b & (Pn::NH - 1);
+          float a[2][4], sq[2];
+#pragma unroll
+          for (int I = 0; I < 2; ++I) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[I][r] = scale * oT[I][r];
+            sq[I] = fmaf(a[I][0], a[I][0], fmaf(a[I][1], a[I][1], fmaf(a[I][2], a[I][2], a[I][3] * a[I][3])));
+          }
+          *reinterpret_cast<u32x4*>(smem + Pn::OFF_HELD + slot * Pn::HELD_SLOT + vw * 1024 + ln * 16) =
+              u32x4{pack_bf16x2(a[0][0], a[0][1]), pack_bf16x2(a[0][2], a[0][3]), pack_bf16x2(a[1][0], a[1][1]),
+                    pack_bf16x2(a[1][2], a[1][3])};
+          float* pw = psum + slot * (32 * Pn::NPART) + ll * Pn::NPART + vw * 4 + lg;
+          pw[0] = sq[0];
+          pw[16 * Pn::NPART] = sq[1];
+        } else if (o) {
           const int c0 = 16 * vw + 4 * lg;
 #pragma unroll
           for (int I = 0; I < NB; ++I) {
@@ -908,7 +1090,11 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         for (int mt = 0; mt < NMT; ++mt) *reinterpret_cast<floatx4*>(stl + mt * 256) = sacc[mt];
         token_block<NMT, SG>(stl, q + tb * K, k + tb * K, v + tb * V, SG ? z + tb : z + tb * K, beta + tb,
                              dt_bias ? dt_bias + (SG ? h : h * K) : nullptr, o ? o + tb * V : nullptr, T, K, V, v0,
-                             vcols, t0c, nval, mult2, scale, ln, 16 * vw + ll);
+                             vcols, t0c, nval, mult2, scale, ln, 16 * vw + ll,
+                             NORM ? reinterpret_cast<bf16_t*>(smem + Pn::OFF_HELD + (b & (Pn::NH - 1)) * Pn::HELD_SLOT +
+                                                              vw * 1024)
+                                  : nullptr,
+                             NORM ? psum + (b & (Pn::NH - 1)) * (32 * Pn::NPART) + vw * 4 : nullptr);
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) sacc[mt] = *reinterpret_cast<const floatx4*>(stl + mt * 256);
         wait_vm();                             // the token path's loads
@@ -936,6 +1122,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       while (s < nck && !slow) {
         int4 f0, f1;                           // flags of block s+1 (stale, and unused, past the end)
         flags_raw(s + 1, f0, f1);
+        if constexpr (NORM) norm_step(s);
         if (vact) vside(std::true_type{}, s, f0, f1);
         lds_barrier();
         slow = s + 1 < nck && any_flag(f0, f1);
@@ -944,11 +1131,19 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       if (s < nck) {
         int4 f0, f1;
         flags_raw(s + 1, f0, f1);
+        if constexpr (NORM) norm_step(s);
         if (vact) vside(std::false_type{}, s, f0, f1);
         lds_barrier();
         slow = s + 1 < nck && any_flag(f0, f1);
         ++s;
       }
+    }
+    if constexpr (NORM) {
+      // the last D blocks (their partial sums were written before the walk's last barrier;
+      // the other tile's waits never depend on this tile's later steps)
+      if (paired && vw == 0 && nck >= 1) norm_export(nck - 1);
+      if (vact)
+        for (int bn = max(0, nck - Pn::D); bn < nck; ++bn) norm_out(bn);
     }
     if (vact && state_out) {
 #pragma unroll
@@ -970,8 +1165,45 @@ hipError_t launch_chunk_fwd_pc_inst(const void* q, const void* k, const void* v,
   const int total = B * H * nvt;
   hipLaunchKernelGGL((chunk_fwd_pc_kernel<KD, VT, C, SG>), dim3(total), dim3(PcCfg<KD, VT, C>::NWAVES * 64), 0, s,
                      (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)z, A_log, dt_bias,
-                     (const bf16_t*)beta, state_in, scale, (bf16_t*)o, state_out, H, T, K, V, nvt, total, 96.0f);
+                     (const bf16_t*)beta, state_in, scale, (bf16_t*)o, state_out, H, T, K, V, nvt, total, 96.0f,
+                     nullptr, 0.0f, nullptr, 0ull, 0, 0);
   return hipGetLastError();
+}
+
+// The forward with the fused output norm (blocks of 32 tokens, 64-column value tiles).
+// With two tiles per head the workgroups of a launch must all be resident (each waits
+// for its partner's sums), so heads go PN_MAX_HEADS per launch, 256 workgroups at most.
+static __global__ void pn_prologue_kernel(unsigned* hdr) {
+  hdr[0] = 0u;                                 // status
+  hdr[1] = hdr[1] + 1u;                        // epoch: no word of an earlier call matches
+}
+
+template <int KD>
+hipError_t launch_chunk_fwd_norm_inst(const void* q, const void* k, const void* v, const void* z, const float* A_log,
+                                      const float* dt_bias, const void* beta, const float* state_in, float scale,
+                                      const float* norm_w, float eps, void* o, float* state_out, int B, int H, int T,
+                                      int K, int V, void* work, unsigned long long spin_ticks, hipStream_t s) {
+  constexpr int VT = 64, C = 32;
+  const int nvt = V > VT ? 2 : 1;
+  const int nheads = B * H;
+  if (nvt == 2) {
+    hipLaunchKernelGGL(pn_prologue_kernel, dim3(1), dim3(1), 0, s, (unsigned*)work);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int per = nvt == 2 ? PN_MAX_HEADS : nheads;
+  for (int head0 = 0; head0 < nheads; head0 += per) {
+    const int nb = min(per, nheads - head0);
+    const int grid = nvt == 2 ? (nb + 7) / 8 * 16 : nb;
+    hipLaunchKernelGGL((chunk_fwd_pc_kernel<KD, VT, C, false, true>), dim3(grid),
+                       dim3(PcCfg<KD, VT, C>::NWAVES * 64), 0, s, (const bf16_t*)q, (const bf16_t*)k,
+                       (const bf16_t*)v, (const bf16_t*)z, A_log, dt_bias, (const bf16_t*)beta, state_in, scale,
+                       (bf16_t*)o, state_out, H, T, K, V, nvt, grid, 96.0f, norm_w, eps, (unsigned char*)work,
+                       spin_ticks, head0, nb);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace kda

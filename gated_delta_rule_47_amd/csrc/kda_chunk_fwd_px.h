@@ -114,14 +114,9 @@ constexpr int PX_MAX_PAIRS = 128;
 constexpr unsigned PX_STATUS_TIMEOUT = 1;   // a wait for the partner's block ran out
 constexpr unsigned PX_STATUS_XCC = 2;       // the two workgroups of a pair are not on one XCD
 
-__device__ __forceinline__ unsigned long long load_b64_dev(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  // device scope (sc1): misses the CU's vector cache, reads L2
-  return __builtin_bit_cast(unsigned long long, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 16));
-}
 __device__ __forceinline__ void store_b64(__amdgpu_buffer_rsrc_t r, unsigned off, unsigned long long x) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, off, 0, 0);
 }
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // 16 bytes per lane from buffer offset `off` into LDS at lds + 16 * lane, device scope.
 __device__ __forceinline__ void dma16_dev(__amdgpu_buffer_rsrc_t r, void* lds, unsigned off) {
@@ -398,7 +393,7 @@ chunk_fwd_px_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
       for (;;) {
         unsigned long long f = want;
-        if (lane < Cfg::NFLAG) f = load_b64_dev(rs_ring, base + lane * 8);
+        if (lane < Cfg::NFLAG) f = __builtin_bit_cast(unsigned long long, load_b64_dev(rs_ring, base + lane * 8));
         if (__ballot(f != want) == 0ull) break;
         if (__builtin_amdgcn_s_memrealtime() - t0 > spin_ticks) {
           give_up(PX_STATUS_TIMEOUT);
@@ -408,7 +403,7 @@ chunk_fwd_px_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       }
       if (!xcc_checked) {
         xcc_checked = true;
-        const unsigned long long x = load_b64_dev(rs_ring, Cfg::RING_XCC + (1 - role) * 8);
+        const unsigned long long x = __builtin_bit_cast(unsigned long long, load_b64_dev(rs_ring, Cfg::RING_XCC + (1 - role) * 8));
         if (x != flag_of((int)my_xcc)) give_up(PX_STATUS_XCC);
       }
     };
@@ -735,7 +730,7 @@ chunk_fwd_px_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         for (int mt = 0; mt < NMT; ++mt) *reinterpret_cast<floatx4*>(stl + mt * 256) = sacc[mt];
         token_block<NMT, SG>(stl, q + tb * K, k + tb * K, v + tb * V, SG ? z + tb : z + tb * K, beta + tb,
                              dt_bias ? dt_bias + (SG ? h : h * K) : nullptr, o ? o + tb * V : nullptr, T, K, V, v0,
-                             VT, t0c, nval, mult2, scale, ln, 16 * vw + ll);
+                             VT, t0c, nval, mult2, scale, ln, 16 * vw + ll, nullptr, nullptr);
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) sacc[mt] = *reinterpret_cast<const floatx4*>(stl + mt * 256);
         wait_vm();

@@ -54,6 +54,16 @@ hipError_t launch_chunk_fwd_px_kd(const void* q, const void* k, const void* v, c
                                   unsigned long long spin_ticks, hipStream_t s);
 size_t px_workspace_bytes(int KD, int nheads);
 
+// The bf16 forward with the output RMSNorm fused into its output stage (o holds
+// y = o / sqrt(mean_v o^2 + eps) * norm_w[h]); when V > 64 the two value tiles of a head
+// exchange per-token sums of squares through `work` (norm_workspace_bytes() of it).
+template <int KD>
+hipError_t launch_chunk_fwd_norm_kd(const void* q, const void* k, const void* v, const void* z, const float* A_log,
+                                    const float* dt_bias, const void* beta, const float* state_in, float scale,
+                                    const float* norm_w, float eps, void* o, float* state_out, int B, int H, int T,
+                                    int K, int V, void* work, unsigned long long spin_ticks, hipStream_t s);
+size_t norm_workspace_bytes(int B, int H, int T, int V);
+
 // Forward tiling actually used for (dtype, K, V, chunk): padded key dim, value tile
 // and the chunk the kernel blocks by.  Returns false when no instance exists.
 struct FwdPlan {

@@ -127,8 +127,48 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* z,
                   void* workspace, size_t workspace_bytes,
                   int B, int H, int T, int K, int V, int dtype, void* stream);
 
-/* Outcome of the last paired kda_chunk_fwd / kda_chunk_fwd_scalar call that used this
- * workspace: synchronizes `stream`, reads the workspace's status word and clears it.
+/* Bytes of device workspace kda_chunk_fwd_norm needs for these sizes: nonzero when
+ * V > 64 (a head's two value tiles exchange per-token sums of squares), 0 otherwise or
+ * on bad sizes or a dtype other than KDA_BF16. */
+size_t kda_chunk_fwd_norm_workspace_bytes(int B, int H, int T, int K, int V, int dtype);
+
+/* kda_chunk_fwd followed by the module's output RMSNorm, fused into the output stage
+ * ("kdafix" page, "Fix 2 -- read scale": the module normalises the read right after
+ * it, which absorbs a constant factor on o, such as the read scale, up to
+ * O(eps / mean(o^2))).  The norm is taken over the V outputs of each token within its
+ * head, with one weight row per head:
+ *   o[b,h,t,:] = r[b,h,t,:] / sqrt(mean_v r[b,h,t,v]^2 + eps) * norm_weight[h,:]
+ * where r = scale * (read) is the output kda_chunk_fwd would store, here kept in fp32
+ * until the division; o is stored as bf16.  Same inputs, state handling, layouts and
+ * checks as kda_chunk_fwd, for KDA_BF16 only (KDA_ERR_DTYPE otherwise); the blocks are
+ * 32 tokens whatever `chunk` (16, 32 or 64) says.
+ *   norm_weight (H,V) f32, or NULL for all ones (a model with one weight shared by all
+ *               heads passes it H times); no output may overlap it.
+ *   eps         >= 0 and finite (KDA_ERR_SHAPE otherwise); with eps = 0 a token whose
+ *               outputs are all zero gives NaN, as the formula does.
+ *   workspace   device buffer of kda_chunk_fwd_norm_workspace_bytes() bytes, 256-byte
+ *               aligned, overlapping no argument; NULL when that size is 0.  It must be
+ *               zero-filled before its first call (hipMemset) and serve this function
+ *               only; each call leaves it ready for the next (every call advances an
+ *               epoch in it, and a word counts only when it carries the current one).
+ *               When V > 64
+ *               the two 64-column tiles of a head run in two workgroups of one XCD,
+ *               which exchange per-token sums of squares through it; two calls in flight
+ *               at once must not share it.  Their waits are bounded
+ *               (kda_set_exchange_timeout_us); if one runs out the call completes, its o
+ *               is undefined and kda_chunk_fwd_status reports KDA_ERR_EXCHANGE.
+ * o must be 8-byte aligned. */
+int kda_chunk_fwd_norm(const void* q, const void* k, const void* v, const void* z,
+                       const float* A_log, const float* dt_bias, const void* beta,
+                       const float* state_in, float scale, int chunk,
+                       const float* norm_weight, float eps,
+                       void* o, float* state_out,
+                       void* workspace, size_t workspace_bytes,
+                       int B, int H, int T, int K, int V, int dtype, void* stream);
+
+/* Outcome of the last call of kda_chunk_fwd / kda_chunk_fwd_scalar (paired) or
+ * kda_chunk_fwd_norm (V > 64) that used this workspace: synchronizes `stream`, reads the
+ * workspace's status word and clears it.
  * KDA_OK, or KDA_ERR_EXCHANGE when a wait between the workgroups of a head ran out or
  * they were not placed on one XCD (that call's outputs are undefined); KDA_ERR_HIP if
  * the synchronization or the copy fails. */

@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 METRIC = "KDA chunked-forward tokens/s (B·H·T/s) + % of roofline, H=32,K=V=128,T=16k"
 METRIC_SCALAR = "KDA chunked-forward tokens/s, scalar-decay gate (kda_chunk_fwd_scalar), H=32,K=V=128,T=16k"
+METRIC_NORM = "KDA chunked-forward tokens/s with the output RMSNorm fused (kda_chunk_fwd_norm), H=32,K=V=128,T=16k"
 
 
 def algorithmic_bytes(wl, scalar_gate=False) -> int:
@@ -43,18 +44,20 @@ def algorithmic_bytes(wl, scalar_gate=False) -> int:
 
 
 KERNEL_SOURCES = ("kda_chunk_fwd_pc.h", "kda_common.h")
-KERNEL_NAME = "kda::chunk_fwd_pc_kernel<128,64,32,false>"
+KERNEL_NAME = "kda::chunk_fwd_pc_kernel<128,64,32,false,false>"
 
 
-def kernel_label(wl, scalar_gate=False, paired=False) -> str:
+def kernel_label(wl, scalar_gate=False, paired=False, norm=False) -> str:
     """The forward instance a kda_chunk_fwd call of this workload launches (the tiling rules
     of the library's forward plan)."""
     C = min(wl.chunk, 32)
+    if norm:
+        return "kda::chunk_fwd_pc_kernel<%d,64,32,false,true>" % max(32, wl.K)
     if paired:
         return "kda::chunk_fwd_px_kernel<%d,%s>" % (max(32, wl.K), str(scalar_gate).lower())
     if wl.dtype == "bf16":
-        return "kda::chunk_fwd_pc_kernel<%d,%d,%d,%s>" % (max(32, wl.K), min(64, max(16, wl.V)), C,
-                                                         str(scalar_gate).lower())
+        return "kda::chunk_fwd_pc_kernel<%d,%d,%d,%s,false>" % (max(32, wl.K), min(64, max(16, wl.V)), C,
+                                                               str(scalar_gate).lower())
     KD = max(16, wl.K)
     VT = min(16 if KD >= 64 else 64, max(16, wl.V))
     return "kda::chunk_fwd_kernel<float,%d,%d,%d>" % (KD, VT, wl.chunk if KD < 128 else C)
@@ -333,6 +336,9 @@ def main():
     ap.add_argument("--scalar-gate", action="store_true",
                     help="time kda_chunk_fwd_scalar instead (one gate input per head-token: channel 0 of the "
                          "workload's z, bias channel 0 of its dt_bias); a separate metric line")
+    ap.add_argument("--norm", action="store_true",
+                    help="time kda_chunk_fwd_norm instead (the forward with the output RMSNorm fused; weight "
+                         "rows 1 + N(0, 0.1^2), eps 1e-6); a separate metric line")
     ap.add_argument("--gate", action="store_true",
                     help="instead of the benchmark, time the standalone gate (kda_gate) on the long workload's z")
     ap.add_argument("--adjoint", action="store_true",
@@ -391,6 +397,17 @@ def main():
     scale = kda.read_scale(wl.K)
 
     fwd = kda.chunk_fwd_scalar if args.scalar_gate else kda.chunk_fwd
+    if args.norm:
+        if args.scalar_gate or wl.dtype != "bf16" or args.paired:
+            raise SystemExit("--norm times the bf16 per-channel-gate forward only")
+        gen = torch.Generator(device=dev).manual_seed(13)
+        norm_w = 1.0 + 0.1 * torch.randn((wl.H, wl.V), device=dev, generator=gen)
+        nws = kda.chunk_fwd_norm_workspace_bytes(wl.B, wl.H, wl.T, wl.K, wl.V)
+        norm_ws = torch.zeros(nws, dtype=torch.uint8, device=dev) if nws else None
+
+        def fwd(q, k, v, z, A_log, dt_bias, beta, state_in, scale, chunk, out, state_out, workspace):
+            return kda.chunk_fwd_norm(q, k, v, z, A_log, dt_bias, beta, state_in, norm_weight=norm_w, eps=1e-6,
+                                      scale=scale, chunk=chunk, out=out, state_out=state_out, workspace=norm_ws)
     # the paired forward's ring (bf16, V = 128): allocated once, outside the timed region
     ws_bytes = 0 if not args.paired else kda.chunk_fwd_workspace_bytes(wl.B, wl.H, wl.T, wl.K, wl.V, wl.chunk, dt)
     workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
@@ -417,6 +434,8 @@ def main():
         raise SystemExit("non-finite output")
     if workspace is not None and kda.chunk_fwd_status(workspace) != 0:
         raise SystemExit("the paired forward reported a failed exchange")
+    if args.norm and norm_ws is not None and kda.chunk_fwd_status(norm_ws) != 0:
+        raise SystemExit("the fused-norm forward reported a failed exchange")
 
     # the copy ceiling, measured after the timed region on the same (warm) GPU
     copy_gbs = copy_bandwidth_gbs(torch)
@@ -424,21 +443,21 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     avg_kernel_ms = float(np.mean(kern_ms))
     tokens = wl.B * wl.H * wl.T
-    nbytes = algorithmic_bytes(wl, args.scalar_gate)
+    nbytes = algorithmic_bytes(wl, args.scalar_gate) + (wl.H * wl.V * 4 if args.norm else 0)
     achieved = nbytes / (avg_kernel_ms * 1e-3) / 1e9
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
             tj = json.load(open(args.traffic_json))
             if (tj.get("workload") == wl.name and tj.get("kernel_source_sha256") == kernel_source_hash()
-                    and not args.chunk and not args.scalar_gate):
+                    and not args.chunk and not args.scalar_gate and not args.norm and not args.paired):
                 traffic = tj.get("bytes_per_launch")
         except Exception:
             traffic = None
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "copy_GBps": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4),
-            "kernel": kernel_label(wl, args.scalar_gate, paired=workspace is not None),
+            "kernel": kernel_label(wl, args.scalar_gate, paired=workspace is not None, norm=args.norm),
             "algorithmic_bytes_per_launch": nbytes,
             "avg_kernel_ms": round(avg_kernel_ms, 4), "min_kernel_ms": round(float(np.min(kern_ms)), 4)}
     cpu = None
@@ -447,7 +466,7 @@ def main():
         print("bench: CPU oracle baseline on %d heads" % workers, file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, n_heads=workers, workers=workers, scalar_gate=args.scalar_gate)
     out = {
-        "metric": ((METRIC_SCALAR if args.scalar_gate else METRIC) if wl.name == "long"
+        "metric": ((METRIC_NORM if args.norm else METRIC_SCALAR if args.scalar_gate else METRIC) if wl.name == "long"
                    else "KDA chunked-forward tokens/s (B·H·T/s), %s workload%s"
                    % (wl.name, ", scalar-decay gate" if args.scalar_gate else "")), "value": round(tokens / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,

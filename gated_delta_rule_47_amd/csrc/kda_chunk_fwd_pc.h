@@ -127,19 +127,26 @@ struct PcCfg {
 // held for D steps (until the other value tile's sums of squares of its tokens have
 // arrived): per block slot, each V wave's 32 x 16 bf16 output tile in its lanes' order
 // (16 bytes per lane) and, per token, 16 partial sums of squares (one per V wave and
-// lane group of 4 columns, contiguous), plus the weight row of the tile.
+// lane group of 4 columns, contiguous), the tile's per-token totals, and the other
+// tile's words for the block (prefetched by DMA); plus the weight row of the tile.
 template <int KD, int VT, int C>
 struct PnCfg {
   using Cfg = PcCfg<KD, VT, C>;
-  static constexpr int D = 3, NH = 4;                 // steps a block is held; slots (> D)
+  static constexpr int D = 4, NH = 5;                 // steps a block is held; slots (> D)
+  static constexpr int NPS = 2;                       // partial-sum slots (folded a step later)
   static constexpr int HELD_SLOT = Cfg::NV * 1024;
   static constexpr int NPART = Cfg::NV * 4;           // partial sums per token
   static constexpr int PSUM_SLOT = 32 * NPART * 4;
   static constexpr int OFF_HELD = round_up(Cfg::TOTAL, 16);
   static constexpr int OFF_PSUM = OFF_HELD + NH * HELD_SLOT;
-  static constexpr int OFF_NW = OFF_PSUM + NH * PSUM_SLOT;
-  static constexpr int TOTAL = OFF_NW + Cfg::VD * 4;
-  static_assert((NH & (NH - 1)) == 0 && NH > D, "norm slots");
+  static constexpr int OFF_NW = OFF_PSUM + NPS * PSUM_SLOT;
+  static constexpr int OFF_WSUM = OFF_NW + Cfg::VD * 4;   // [slot][32] fp32 totals
+  static constexpr int TOTAL = OFF_WSUM + NH * 32 * 4;
+  // (the prefetched words, [slot][32] x 8 bytes, are an LDS object of their own: a DMA in
+  // flight into them then holds up no other LDS access of the issuing wave)
+  static constexpr int PW_WORDS = NH * 32;
+  static_assert(NH > D, "norm slots");
+  __device__ static int slot(int b) { return b % NH; }
 };
 
 // Workspace of the fused norm when a head has two value tiles: a header (word 0: status,
@@ -359,13 +366,14 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   using Cfg = PcCfg<KD, VT, C>;
   using Pn = PnCfg<KD, VT, C>;
   constexpr int SMEM = NORM ? Pn::TOTAL : Cfg::TOTAL;
-  static_assert(!NORM || (C == 32 && Pn::TOTAL <= 160 * 1024), "norm: 32-token blocks, LDS budget");
+  static_assert(!NORM || (C == 32 && Pn::TOTAL + Pn::PW_WORDS * 8 <= 160 * 1024), "norm: 32-token blocks, LDS budget");
   constexpr int CD = Cfg::CD, NB = Cfg::NB, NNT = Cfg::NNT, NMT = Cfg::NMT;
   constexpr int LD_TK = Cfg::LD_TK, LD_CT = Cfg::LD_CT, LD_A = Cfg::LD_A;
   constexpr int NS = KD / 32;                         // 32-deep channel slices
   constexpr int NTHR = Cfg::NWAVES * 64;
 
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  __shared__ __attribute__((aligned(16))) u32x2 s_pw[NORM ? Pn::PW_WORDS : 1];
   float* sA = reinterpret_cast<float*>(smem + Cfg::OFF_A);
   int* sFlag = reinterpret_cast<int*>(smem + Cfg::OFF_FLAG);   // [block % 3][E wave]
   // Buffer offsets of block b, passed through an empty asm so that the compiler keeps them
@@ -865,40 +873,74 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       const size_t row = (size_t)nck * 256;
       return make_rsrc(work + PN_HEADER + ((size_t)bh * 2 + tile) * row, (unsigned)row);
     };
-    // Wave 0 publishes this tile's per-token sums of squares of block b (the V waves wrote
-    // their partial sums during step b): one 8-byte store per token, sum and epoch together.
-    auto norm_export = [&](int b) __attribute__((always_inline)) {
-      const float* ps = psum + (b & (Pn::NH - 1)) * (32 * Pn::NPART);
-      if (lane < 32) {
-        float t = 0.0f;
+    float* const wsum = reinterpret_cast<float*>(smem + Pn::OFF_WSUM);
+    u32x2* const pwd = s_pw;
+    // per-token total of this tile's partial sums of block b
+    auto tile_sum = [&](int b, int t) __attribute__((always_inline)) {
+      const float* ps = psum + (b & (Pn::NPS - 1)) * (32 * Pn::NPART) + t * Pn::NPART;
+      float x = 0.0f;
 #pragma unroll
-        for (int w = 0; w < Pn::NPART; w += 4) {
-          const floatx4 x = *reinterpret_cast<const floatx4*>(ps + lane * Pn::NPART + w);
-          t += (x[0] + x[1]) + (x[2] + x[3]);
-        }
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(t), epoch}, ring_rsrc(role),
-                                              (unsigned)((b * 32 + lane) * 8), 0, 0);
+      for (int w = 0; w < Pn::NPART; w += 4) {
+        const floatx4 y = *reinterpret_cast<const floatx4*>(ps + w);
+        x += (y[0] + y[1]) + (y[2] + y[3]);
       }
+      return x;
+    };
+    // Wave 0 at step b+1: the tile's per-token sums of squares of block b (the V waves wrote
+    // their partial sums during step b) into LDS, and, with two tiles, to the workspace: one
+    // 8-byte store per token, sum and epoch together.
+    auto norm_export = [&](int b) __attribute__((always_inline)) {
+      if (lane < 32) {
+        const float t = tile_sum(b, lane);
+        wsum[Pn::slot(b) * 32 + lane] = t;
+        if (paired)
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(t), epoch}, ring_rsrc(role),
+                                                (unsigned)((b * 32 + lane) * 8), 0, 0);
+      }
+    };
+    // Wave 0 at the end of step b+2: the other tile's words of block b (published at the
+    // start of its step b+1) into LDS (DMA, device scope); waited for at the end of step
+    // b+3, before its barrier; read at the end of step b+4.
+    auto norm_prefetch = [&](int b) __attribute__((always_inline)) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ring_rsrc(1 - role),
+                                               (__attribute__((address_space(3))) void*)(pwd + Pn::slot(b) * 32),
+                                               4, (unsigned)(b * 256 + lane * 4), 0, 0, 16);
     };
     // y = o / sqrt(mean(o^2) + eps) * w for the held block bn: the sums of this tile from
     // LDS, those of the other tile from its words (waiting, bounded, until both of the
     // lane's words carry this call's epoch), then the stores.
-    auto norm_out = [&](int bn) __attribute__((always_inline)) {
-      const int slot = bn & (Pn::NH - 1);
+    // own: this tile's totals are in LDS (exported before a barrier); else summed here.
+    // pre: the other tile's words were prefetched into LDS; else (or if they were not yet
+    // there) they are read, and waited for, directly.
+    auto norm_out = [&](int bn, bool own, bool pre) __attribute__((always_inline)) {
+      const int slot = Pn::slot(bn);
       const int lg = lane >> 4, ll = lane & 15;
-      const float* ps = psum + slot * (32 * Pn::NPART);
-      float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-      for (int w = 0; w < Pn::NPART; w += 4) {
-        const floatx4 x0 = *reinterpret_cast<const floatx4*>(ps + ll * Pn::NPART + w);
-        const floatx4 x1 = *reinterpret_cast<const floatx4*>(ps + (16 + ll) * Pn::NPART + w);
-        s0 += (x0[0] + x0[1]) + (x0[2] + x0[3]);
-        s1 += (x1[0] + x1[1]) + (x1[2] + x1[3]);
+      float s0, s1;
+      if (own) {
+        s0 = wsum[slot * 32 + ll];
+        s1 = wsum[slot * 32 + 16 + ll];
+      } else {
+        s0 = tile_sum(bn, ll);
+        s1 = tile_sum(bn, 16 + ll);
       }
       if (paired) {
         const __amdgpu_buffer_rsrc_t rp = ring_rsrc(1 - role);
         const unsigned off0 = (unsigned)((bn * 32 + ll) * 8), off1 = off0 + 128;
-        u32x2 a = load_b64_dev(rp, off0), c = load_b64_dev(rp, off1);
+        u32x2 a, c;
+        if (pre) {
+          // (through asm: the compiler would make these reads wait for the DMA into the
+          // next slot, which is still in flight and which they do not touch)
+          const unsigned pa =
+              (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)(pwd + slot * 32 + ll);
+          asm volatile("ds_read_b64 %0, %2\n\tds_read_b64 %1, %2 offset:128\n\ts_waitcnt lgkmcnt(0)"
+                       : "=&v"(a), "=&v"(c)
+                       : "v"(pa)
+                       : "memory");
+        }
+        if (!pre || (!dead && __ballot(a.y != epoch || c.y != epoch) != 0ull)) {
+          a = load_b64_dev(rp, off0);
+          c = load_b64_dev(rp, off1);
+        }
         // (a zero bound gives up at once, whether or not the words are there yet)
         if (!dead && (spin_ticks == 0 || __ballot(a.y != epoch || c.y != epoch) != 0ull)) {
           dead = spin_ticks == 0;
@@ -935,10 +977,22 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           __builtin_amdgcn_raw_buffer_store_b64(y1, rs_o, (unsigned)(((bn * C + 16 + ll) * V + v0 + c0) * 2), 0, 0);
       }
     };
-    // at the start of step s: publish block s-1, finish block s-D
+    // at the start of step s: publish block s-1, prefetch the other tile's words of block
+    // s-2, finish block s-3
+    // Step s: at its start wave 0 publishes block s-1 (partial sums written during step
+    // s-1).  At its end (where the plain forward stores its output) wave 0 first waits for
+    // the prefetch of block s-3 (issued a step earlier; its own stores of this step are
+    // not issued yet, so the wait costs nothing), the V waves finish block s-4, and wave 0
+    // starts the prefetch of block s-2.  The exchange so tolerates about two steps of
+    // drift between the two workgroups.
+    static_assert(!NORM || Pn::D == 4, "the step schedule assumes a 4-step hold");
     auto norm_step = [&](int s) __attribute__((always_inline)) {
-      if (paired && vw == 0 && s >= 1) norm_export(s - 1);
-      if (vact && s >= Pn::D) norm_out(s - Pn::D);
+      if (vw == 0 && s >= 1) norm_export(s - 1);
+    };
+    auto norm_end = [&](int s) __attribute__((always_inline)) {
+      if (paired && vw == 0) wait_vm();
+      if (vact && s >= Pn::D) norm_out(s - Pn::D, true, paired);
+      if (paired && vw == 0 && s >= 2) norm_prefetch(s - 2);
     };
 
     // nf0, nf1: the raw slow flags of block b+1, loaded at the top of the step and only
@@ -1057,7 +1111,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           // held for the norm: the scaled outputs as bf16, and the per-token sums of
           // squares over this wave's 16 columns taken before rounding
           static_assert(!NORM || NB == 2, "norm blocks are 32 tokens");
-          const int slot = b & (Pn::NH - 1);
+          const int slot = Pn::slot(b);
           float a[2][4], sq[2];
 #pragma unroll
           for (int I = 0; I < 2; ++I) {
@@ -1068,7 +1122,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           *reinterpret_cast<u32x4*>(smem + Pn::OFF_HELD + slot * Pn::HELD_SLOT + vw * 1024 + ln * 16) =
               u32x4{pack_bf16x2(a[0][0], a[0][1]), pack_bf16x2(a[0][2], a[0][3]), pack_bf16x2(a[1][0], a[1][1]),
                     pack_bf16x2(a[1][2], a[1][3])};
-          float* pw = psum + slot * (32 * Pn::NPART) + ll * Pn::NPART + vw * 4 + lg;
+          float* pw = psum + (b & (Pn::NPS - 1)) * (32 * Pn::NPART) + ll * Pn::NPART + vw * 4 + lg;
           pw[0] = sq[0];
           pw[16 * Pn::NPART] = sq[1];
         } else if (o) {
@@ -1091,10 +1145,10 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         token_block<NMT, SG>(stl, q + tb * K, k + tb * K, v + tb * V, SG ? z + tb : z + tb * K, beta + tb,
                              dt_bias ? dt_bias + (SG ? h : h * K) : nullptr, o ? o + tb * V : nullptr, T, K, V, v0,
                              vcols, t0c, nval, mult2, scale, ln, 16 * vw + ll,
-                             NORM ? reinterpret_cast<bf16_t*>(smem + Pn::OFF_HELD + (b & (Pn::NH - 1)) * Pn::HELD_SLOT +
+                             NORM ? reinterpret_cast<bf16_t*>(smem + Pn::OFF_HELD + Pn::slot(b) * Pn::HELD_SLOT +
                                                               vw * 1024)
                                   : nullptr,
-                             NORM ? psum + (b & (Pn::NH - 1)) * (32 * Pn::NPART) + vw * 4 : nullptr);
+                             NORM ? psum + (b & (Pn::NPS - 1)) * (32 * Pn::NPART) + vw * 4 : nullptr);
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) sacc[mt] = *reinterpret_cast<const floatx4*>(stl + mt * 256);
         wait_vm();                             // the token path's loads
@@ -1124,6 +1178,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         flags_raw(s + 1, f0, f1);
         if constexpr (NORM) norm_step(s);
         if (vact) vside(std::true_type{}, s, f0, f1);
+        if constexpr (NORM) norm_end(s);
         lds_barrier();
         slow = s + 1 < nck && any_flag(f0, f1);
         ++s;
@@ -1133,6 +1188,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         flags_raw(s + 1, f0, f1);
         if constexpr (NORM) norm_step(s);
         if (vact) vside(std::false_type{}, s, f0, f1);
+        if constexpr (NORM) norm_end(s);
         lds_barrier();
         slow = s + 1 < nck && any_flag(f0, f1);
         ++s;
@@ -1141,9 +1197,10 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     if constexpr (NORM) {
       // the last D blocks (their partial sums were written before the walk's last barrier;
       // the other tile's waits never depend on this tile's later steps)
-      if (paired && vw == 0 && nck >= 1) norm_export(nck - 1);
+      if (vw == 0 && nck >= 1) norm_export(nck - 1);
       if (vact)
-        for (int bn = max(0, nck - Pn::D); bn < nck; ++bn) norm_out(bn);
+        for (int bn = max(0, nck - Pn::D); bn < nck; ++bn)
+          norm_out(bn, bn + 1 < nck, paired && bn + 3 < nck);
     }
     if (vact && state_out) {
 #pragma unroll

@@ -294,9 +294,12 @@ static int recurrent_step_impl(const void* q, const void* k, const void* v, cons
   const size_t es = esize(dtype);
   const size_t nk = (size_t)B * H * K * es, nv = (size_t)B * H * V * es, ns = (size_t)B * H * K * V * 4;
   const size_t nz = zc ? nk : (size_t)B * H * es;
+  const size_t nbe = (size_t)B * H * es, na = (size_t)H * 4, ndb = (size_t)H * (zc ? K : 1) * 4;
   if (overlap(o, nv, q, nk) || overlap(o, nv, k, nk) || overlap(o, nv, z, nz) || overlap(o, nv, v, nv) ||
-      overlap(o, nv, beta, (size_t)B * H * es) || overlap(o, nv, state, ns) || overlap(state, ns, q, nk) ||
-      overlap(state, ns, k, nk) || overlap(state, ns, z, nz) || overlap(state, ns, v, nv))
+      overlap(o, nv, beta, nbe) || overlap(o, nv, state, ns) || overlap(o, nv, A_log, na) ||
+      overlap(o, nv, dt_bias, ndb) || overlap(state, ns, q, nk) || overlap(state, ns, k, nk) ||
+      overlap(state, ns, z, nz) || overlap(state, ns, v, nv) || overlap(state, ns, beta, nbe) ||
+      overlap(state, ns, A_log, na) || overlap(state, ns, dt_bias, ndb))
     return reject(KDA_ERR_ALIAS);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dtype == KDA_BF16

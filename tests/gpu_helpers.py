@@ -1,6 +1,8 @@
 """Shared helpers of the GPU parity tests: device upload of the seeded inputs and
 per-head oracle evaluation.  Nothing here computes any part of the method: the
 expected values always come from oracle/."""
+import json
+import os
 import sys
 
 import numpy as np
@@ -16,6 +18,23 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}   # max|x - ref| / max|ref| per tensor
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def check(name, got, ref, tol):
+    """rel_err of one output tensor against the oracle, asserted against its bar.  When
+    the environment variable KDA_MARGINS_OUT names a file, one JSON line per check is
+    appended to it (test id, tensor, rel_err, bar): the parity margins summary is built
+    from those lines (tests/margins_table.py)."""
+    e = R.rel_err(got, ref)
+    say("  %-10s rel_err %.3e (bar %.0e)" % (name, e, tol))
+    out = os.environ.get("KDA_MARGINS_OUT")
+    if out:
+        test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+        with open(out, "a") as f:
+            f.write(json.dumps({"test": test, "tensor": name, "rel_err": e, "bar": tol,
+                                "finite": bool(np.all(np.isfinite(got)))}) + "\n")
+    assert np.all(np.isfinite(got)), name
+    assert e <= tol, (name, e)
 
 
 def to_dev(x, dtype):

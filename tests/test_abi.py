@@ -118,6 +118,13 @@ def test_argument_errors_before_launch():
     assert lib.kda_recurrent_step(q, k, v, z, A, dt, b, None, 0.1, o, 1, 1, 8, 8, 0, None) == -1
     assert lib.kda_recurrent_step(q, k, v, z, A, dt, b, s_in, 0.1, o, 1, 1, 8, 24, 0, None) == -2
     assert lib.kda_recurrent_step(q, k, v, z, A, dt, b, s_in, 0.1, q, 1, 1, 8, 8, 0, None) == -5
+    # the state overlapping beta, A_log or dt_bias; o overlapping A_log (decode step), and
+    # the forward's outputs overlapping A_log or dt_bias: each written while still read
+    assert lib.kda_recurrent_step(q, k, v, z, A, dt, b, b, 0.1, o, 1, 1, 8, 8, 0, None) == -5
+    assert lib.kda_recurrent_step(q, k, v, z, A, dt, b, A, 0.1, o, 1, 1, 8, 8, 0, None) == -5
+    assert lib.kda_recurrent_step(q, k, v, z, A, dt, b, s_in, 0.1, dt, 1, 1, 8, 8, 0, None) == -5
+    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, A, s_out, None, 0, 1, 1, 16, 8, 8, 0, None) == -5
+    assert lib.kda_chunk_fwd(q, k, v, z, A, dt, b, s_in, 0.1, 64, o, dt, None, 0, 1, 1, 16, 8, 8, 0, None) == -5
     # gate
     assert lib.kda_gate(None, A, dt, o, None, 1, 1, 4, 8, 0, None) == -1
     assert lib.kda_gate(z, A, dt, z, None, 1, 1, 4, 8, 0, None) == -5
@@ -152,7 +159,7 @@ def test_argument_errors_before_launch():
     assert lib.kda_gate_bwd_noalloc(z, A, dt, g[0], o, None, None, 2, 1, 16384 * 128 + 1, 128, 0, None) == -10
     rej1 = (ctypes.c_ulonglong * 6)()
     lib.kda_get_counters(rej1, 6)
-    assert rej1[4] - rej0[4] == 35 and list(rej1[:4]) == list(rej0[:4]) and rej1[5] == rej0[5]
+    assert rej1[4] - rej0[4] == 40 and list(rej1[:4]) == list(rej0[:4]) and rej1[5] == rej0[5]
 
 
 @pytest.mark.skipif(_gpu_visible(), reason="fake device pointers: CPU-only check")

@@ -27,9 +27,11 @@ def test_forward_flops_per_head_token():
 
 def test_kernel_labels_follow_the_forward_plan():
     W = ks.WORKLOADS
-    assert bench.kernel_label(W["long"]) == bench.KERNEL_NAME == "kda::chunk_fwd_pc_kernel<128,64,32,false>"
-    assert bench.kernel_label(W["long"], True) == "kda::chunk_fwd_pc_kernel<128,64,32,true>"
-    assert bench.kernel_label(W["nano"]) == "kda::chunk_fwd_pc_kernel<64,64,32,false>"
+    assert bench.kernel_label(W["long"]) == bench.KERNEL_NAME == "kda::chunk_fwd_pc_kernel<128,64,32,false,false>"
+    assert bench.kernel_label(W["long"], True) == "kda::chunk_fwd_pc_kernel<128,64,32,true,false>"
+    assert bench.kernel_label(W["long"], norm=True) == "kda::chunk_fwd_pc_kernel<128,64,32,false,true>"
+    assert bench.kernel_label(W["nano"]) == "kda::chunk_fwd_pc_kernel<64,64,32,false,false>"
+    assert bench.block_tokens(W["long"]) == 32 and bench.block_tokens(W["tiny"]) == 16
     assert bench.kernel_label(W["tiny"]) == "kda::chunk_fwd_kernel<float,16,16,16>"
     assert bench.kernel_label(W["adjoint"]) == "kda::chunk_fwd_kernel<float,128,16,32>"
 

@@ -18,7 +18,7 @@ import gated_delta_rule_47_amd as kda
 import kda_synth as ks
 from oracle import kda_ref as R
 
-from gpu_helpers import DEV, TOL, host, oracle_heads, oracle_heads_from_slices, say, to_dev, upload
+from gpu_helpers import check, DEV, TOL, host, oracle_heads, oracle_heads_from_slices, say, to_dev, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -26,11 +26,7 @@ KDA_ERR_EXCHANGE = -9
 EPS = 1e-5
 
 
-def _check(name, got, ref, tol):
-    e = R.rel_err(got, ref)
-    say("  %-10s rel_err %.3e (bar %.0e)" % (name, e, tol))
-    assert np.all(np.isfinite(got)), name
-    assert e <= tol, (name, e)
+_check = check
 
 
 def _weight(H, V, seed=9):

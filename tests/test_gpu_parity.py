@@ -13,7 +13,7 @@ import gated_delta_rule_47_amd as kda
 import kda_synth as ks
 from oracle import kda_ref as R
 
-from gpu_helpers import DEV, TOL, act_dtype, host, oracle_heads, oracle_heads_from_slices, say, to_dev, upload
+from gpu_helpers import check, DEV, TOL, act_dtype, host, oracle_heads, oracle_heads_from_slices, say, to_dev, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -23,11 +23,7 @@ def _fwd(d, chunk, scale=None, state_in=True):
                          d["state_in"] if state_in else None, scale=scale, chunk=chunk)
 
 
-def _check(name, got, ref, tol):
-    e = R.rel_err(got, ref)
-    say("  %-10s rel_err %.3e (bar %.0e)" % (name, e, tol))
-    assert np.all(np.isfinite(got)), name
-    assert e <= tol, (name, e)
+_check = check
 
 
 # ----------------------------------------------------------------------------- gate
@@ -70,6 +66,54 @@ def test_recurrent_step_matches_token_recurrence(wl_name, T):
     _check("state", host(S).reshape(1, -1, wl.K, wl.V), S_ref, 1e-4)
 
 
+def _decode(d, T0, T1):
+    """Tokens T0 .. T1-1 through the decode step, from the state in d["S"] (updated)."""
+    os_ = []
+    for t in range(T0, T1):
+        os_.append(kda.recurrent_step(d["q"][:, :, t].contiguous(), d["k"][:, :, t].contiguous(),
+                                      d["v"][:, :, t].contiguous(), d["z"][:, :, t].contiguous(),
+                                      d["A_log"], d["dt_bias"], d["beta"][:, :, t].contiguous(), d["S"]))
+    return torch.stack(os_, dim=2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_recurrent_step_k128(dtype):
+    """The decode step at K = V = 128 (two 64-column value tiles per head), fp32 and bf16
+    activations, 40 tokens against the token recurrence."""
+    base = ks.WORKLOADS["layer"] if dtype == "f32" else ks.WORKLOADS["nano"]
+    wl = base.with_(B=2, H=3, K=128, V=128, state="normal:0.1")
+    T = 40
+    x = ks.generate(wl, T=T)
+    d = upload(wl, x)
+    d["S"] = d["state_in"].clone()
+    o = _decode(d, 0, T)
+    o_ref, S_ref = oracle_heads(wl, x, [(b, h) for b in range(2) for h in range(3)])
+    say("decode K=V=128", dtype)
+    _check("o", host(o).reshape(1, 6, T, 128), o_ref, TOL[wl.dtype])
+    _check("state", host(d["S"]).reshape(1, 6, 128, 128), S_ref, 1e-4)
+
+
+def test_prefill_decode_handoff_long_workload():
+    """The long workload's shape (B=4, H=32, K=V=128, bf16): the chunked forward over the
+    first 16380 tokens, then the decode step for the last 4 from its final state, on the
+    whole batch; eight heads (one per XCD) against the oracle over all 16384 tokens."""
+    wl = ks.WORKLOADS["long"]
+    T, Tp = wl.T, wl.T - 4
+    say("generating long")
+    x = ks.generate(wl)
+    d = upload(wl, x)
+    del x
+    o_p, S_p = kda.chunk_fwd(*(d[n][:, :, :Tp].contiguous() for n in ("q", "k", "v", "z")), d["A_log"],
+                             d["dt_bias"], d["beta"][:, :, :Tp].contiguous(), d["state_in"], chunk=wl.chunk)
+    d["S"] = S_p
+    o_d = _decode(d, Tp, T)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_heads_from_slices(wl, LONG_HEADS)
+    _check("o prefill", np.stack([host(o_p[b, h]) for b, h in LONG_HEADS])[None], o_ref[:, :, :Tp], TOL["bf16"])
+    _check("o decode", np.stack([host(o_d[b, h]) for b, h in LONG_HEADS])[None], o_ref[:, :, Tp:], TOL["bf16"])
+    _check("state", np.stack([host(d["S"][b, h]) for b, h in LONG_HEADS])[None], S_ref, TOL["bf16"])
+
+
 # ----------------------------------------------------------------------------- chunked forward
 @pytest.mark.parametrize("wl_name", ["tiny", "layer"])
 def test_chunk_fwd_fp32_workloads(wl_name):
@@ -94,8 +138,13 @@ def test_chunk_fwd_nano_short_all_heads():
     _check("state", host(S).reshape(1, -1, wl.K, wl.V), S_ref, TOL["bf16"])
 
 
-@pytest.mark.parametrize("wl_name,heads", [("nano", [(0, 0), (3, 5), (7, 7)]),
-                                           ("long", [(0, 0), (2, 17), (3, 31)])])
+# Sampled heads, one per XCD: the forward runs workgroup x on XCD x % 8 and maps the
+# value tiles of head bh to XCD bh // (heads / 8) (both tiles of a head on one XCD).
+NANO_HEADS = [(0, 0), (1, 3), (2, 6), (3, 1), (4, 4), (5, 7), (6, 2), (7, 5)]        # bh // 8 = 0..7
+LONG_HEADS = [(0, 0), (0, 21), (1, 10), (1, 31), (2, 4), (2, 25), (3, 14), (3, 19)]  # bh // 16 = 0..7
+
+
+@pytest.mark.parametrize("wl_name,heads", [("nano", NANO_HEADS), ("long", LONG_HEADS)])
 def test_chunk_fwd_full_size_sampled_heads(wl_name, heads):
     """The full workload, launched exactly as the benchmark launches it; the oracle
     recomputes a few heads from their regenerated slices."""
@@ -112,6 +161,23 @@ def test_chunk_fwd_full_size_sampled_heads(wl_name, heads):
     Sg = np.stack([host(S[b, h]) for b, h in heads])[None]
     _check("o", og, o_ref, TOL["bf16"])
     _check("state", Sg, S_ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("T", [1024, 4096])
+def test_chunk_fwd_long_error_growth_with_T(T):
+    """bf16 error against the sequence length at the long workload's shape (B=4, H=32,
+    K=V=128): T = 1k and 4k here, 16k in the full-size test, on the same eight heads (one
+    per XCD).  The fp32 state carries the whole sequence, so a drift of the carried
+    state would show as growth with T."""
+    wl = ks.WORKLOADS["long"]
+    x = ks.generate(wl, T=T)
+    d = upload(wl, x)
+    o, S = _fwd(d, wl.chunk)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_heads(wl, x, LONG_HEADS)
+    say("long, T =", T)
+    _check("o", np.stack([host(o[b, h]) for b, h in LONG_HEADS])[None], o_ref, TOL["bf16"])
+    _check("state", np.stack([host(S[b, h]) for b, h in LONG_HEADS])[None], S_ref, TOL["bf16"])
 
 
 CASES = [  # (dtype, K, V, chunk, T)
@@ -252,7 +318,7 @@ def test_chunk_bwd_adjoint_workload_sampled_heads():
     d = upload(wl, x)
     gr = _bwd(d, wl.chunk)
     torch.cuda.synchronize()
-    heads = [(0, 0), (1, 15)]
+    heads = [(0, 0), (0, 7), (1, 8), (1, 15)]
     ref = _oracle_bwd(wl, x, heads)
     for n in GRADS:
         got = np.stack([host(gr[n][b, h]) for b, h in heads])[None]

@@ -15,16 +15,12 @@ import gated_delta_rule_47_amd as kda
 import kda_synth as ks
 from oracle import kda_ref as R
 
-from gpu_helpers import TOL, act_dtype, host, say, to_dev, upload
+from gpu_helpers import check, TOL, act_dtype, host, say, to_dev, upload
 
 pytestmark = pytest.mark.gpu
 
 
-def _check(name, got, ref, tol):
-    e = R.rel_err(got, ref)
-    say("  %-10s rel_err %.3e (bar %.0e)" % (name, e, tol))
-    assert np.all(np.isfinite(got)), name
-    assert e <= tol, (name, e)
+_check = check
 
 
 def _scalar_inputs(wl, x):

@@ -376,8 +376,8 @@ int kda_recurrent_step_scalar(const void* q, const void* k, const void* v, const
 }
 
 size_t kda_chunk_bwd_workspace_bytes(int B, int H, int T, int K, int V, int chunk) {
-  if (B < 1 || H < 1 || T < 0) return 0;
-  return bwd_workspace_bytes(B, H, T, K, V, chunk);
+  if (B < 1 || H < 1 || T < 0 || !valid_dim(K) || !valid_dim(V) || !valid_chunk(chunk)) return 0;
+  return chunk_bwd_mfma_workspace_bytes(B, H, T, K, V);
 }
 
 int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z, const float* A_log,
@@ -392,8 +392,10 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z, co
   if (B < 1 || H < 1 || T < 0 || !valid_dim(K) || !valid_dim(V)) return reject(KDA_ERR_SHAPE);
   if (!valid_chunk(chunk)) return reject(KDA_ERR_CHUNK);
   if ((size_t)(T + 64) * (size_t)(K > V ? K : V) * 4 > 0x7fffffffu) return reject(KDA_ERR_SHAPE);
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)z) & 7) return reject(KDA_ERR_ALIGN);
-  const size_t need = bwd_workspace_bytes(B, H, T, K, V, chunk);
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)z) & 7) return reject(KDA_ERR_ALIGN);
+  if (((uintptr_t)v | (uintptr_t)d_o) & 15) return reject(KDA_ERR_ALIGN);   // read in 16-byte pieces
+  if ((long long)B * H > 65535) return reject(KDA_ERR_SHAPE);   // one grid row per head
+  const size_t need = chunk_bwd_mfma_workspace_bytes(B, H, T, K, V);
   if (!workspace || workspace_bytes < need) return reject(KDA_ERR_WORKSPACE);
   if ((uintptr_t)workspace & 15) return reject(KDA_ERR_ALIGN);
   const size_t nk = (size_t)B * H * T * K * 4, nv = (size_t)B * H * T * V * 4, nb = (size_t)B * H * T * 4;
@@ -408,9 +410,10 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z, co
     for (const Buf& b : outs)
       if (&a != &b && overlap(a.p, a.n, b.p, b.n)) return reject(KDA_ERR_ALIAS);
   }
-  hipError_t e = launch_chunk_bwd((const float*)q, (const float*)k, (const float*)v, (const float*)z, A_log, dt_bias,
-                                  (const float*)beta, state_in, scale, chunk, (const float*)d_o, d_state_out, dq, dk,
-                                  dv, dg, dbeta, dstate_in, workspace, B, H, T, K, V, (hipStream_t)stream);
+  hipError_t e = launch_chunk_bwd_mfma((const float*)q, (const float*)k, (const float*)v, (const float*)z, A_log,
+                                       dt_bias, (const float*)beta, state_in, scale, (const float*)d_o, d_state_out,
+                                       dq, dk, dv, dg, dbeta, dstate_in, workspace, B, H, T, K, V,
+                                       (hipStream_t)stream);
   if (e != hipSuccess) return reject(KDA_ERR_HIP);
   g_counters[KDA_COUNTER_CHUNK_BWD].fetch_add(1, std::memory_order_relaxed);
   return KDA_OK;

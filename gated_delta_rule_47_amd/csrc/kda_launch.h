@@ -71,12 +71,13 @@ struct FwdPlan {
 };
 bool fwd_plan(bool bf16, int K, int V, int chunk, FwdPlan* plan);
 
-// Adjoint (fp32 activations).
-size_t bwd_workspace_bytes(int B, int H, int T, int K, int V, int chunk);
-hipError_t launch_chunk_bwd(const float* q, const float* k, const float* v, const float* z, const float* A_log,
-                            const float* dt_bias, const float* beta, const float* state_in, float scale, int chunk,
-                            const float* d_o, const float* d_state_out, float* dq, float* dk, float* dv, float* dg,
-                            float* dbeta, float* dstate_in, void* workspace, int B, int H, int T, int K, int V,
-                            hipStream_t s);
+// Chunked adjoint on MFMA (fp32 activations), see kda_bwd_chunk.hip.
+size_t chunk_bwd_mfma_workspace_bytes(int B, int H, int T, int K, int V);
+hipError_t launch_chunk_bwd_mfma(const float* q, const float* k, const float* v, const float* z, const float* A_log,
+                                 const float* dt_bias, const float* beta, const float* state_in, float scale,
+                                 const float* d_o, const float* d_state_out, float* dq, float* dk, float* dv,
+                                 float* dg, float* dbeta, float* dstate_in, void* workspace, int B, int H, int T,
+                                 int K, int V, hipStream_t s);
+
 
 }  // namespace kda

@@ -312,6 +312,26 @@ def test_chunk_bwd_small(K, V, chunk, T, with_ds):
         _check(n, got, ref[n], 1e-4)
 
 
+@pytest.mark.parametrize("T", [1, 150])
+def test_chunk_bwd_saturated_gates_take_the_token_path(T):
+    """Heads whose decay inside a 32-token chunk leaves the factorised form's range
+    (A_log = 20 and 8, and a run of large z on a third head) are evaluated token by token
+    in the reverse and gradient passes; the heads next to them keep the MFMA path."""
+    wl = ks.WORKLOADS["adjoint"].with_(B=1, H=4, a_log="list:20,-3,8,0")
+    x = ks.generate(wl, T=T)
+    if T > 70:
+        x["z"][0, 2, 40:70] += 6.0
+    d = upload(wl, x)
+    dso = np.random.default_rng(8).standard_normal((1, 4, wl.K, wl.V)).astype(np.float32)
+    gr = _bwd(d, wl.chunk, to_dev(dso, torch.float32))
+    heads = [(0, h) for h in range(4)]
+    ref = _oracle_bwd(wl, x, heads, dso)
+    say("saturated adjoint, T =", T)
+    for n in GRADS:
+        got = host(gr[n]).reshape(ref[n].shape)
+        _check(n, got, ref[n], 1e-4)
+
+
 def test_chunk_bwd_adjoint_workload_sampled_heads():
     wl = ks.WORKLOADS["adjoint"]
     x = ks.generate(wl)

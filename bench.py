@@ -303,7 +303,7 @@ def adjoint_bench(steps, warmup):
                       "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": FP32_PEAK_TFLOPS,
                                    "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 5),
                                    "algorithmic_flops_per_call": flops, "algorithmic_bytes_per_call": nbytes,
-                                   "note": "whole call (checkpointing forward, reverse walk, tile reduction), "
+                                   "note": "whole call (prep, forward and reverse passes over the chunks, gradient pass), "
                                            "HIP events on the launch stream"}}))
 
 

@@ -392,8 +392,9 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z, co
   if (B < 1 || H < 1 || T < 0 || !valid_dim(K) || !valid_dim(V)) return reject(KDA_ERR_SHAPE);
   if (!valid_chunk(chunk)) return reject(KDA_ERR_CHUNK);
   if ((size_t)(T + 64) * (size_t)(K > V ? K : V) * 4 > 0x7fffffffu) return reject(KDA_ERR_SHAPE);
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)z) & 7) return reject(KDA_ERR_ALIGN);
-  if (((uintptr_t)v | (uintptr_t)d_o) & 15) return reject(KDA_ERR_ALIGN);   // read in 16-byte pieces
+  if ((uintptr_t)z & 7) return reject(KDA_ERR_ALIGN);
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)d_o) & 15)
+    return reject(KDA_ERR_ALIGN);   // read in 16-byte pieces
   if ((long long)B * H > 65535) return reject(KDA_ERR_SHAPE);   // one grid row per head
   const size_t need = chunk_bwd_mfma_workspace_bytes(B, H, T, K, V);
   if (!workspace || workspace_bytes < need) return reject(KDA_ERR_WORKSPACE);

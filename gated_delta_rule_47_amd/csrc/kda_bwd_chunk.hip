@@ -102,7 +102,9 @@ prep_kernel(const float* __restrict__ q, const float* __restrict__ k, const floa
   using Rc = Rec<KD>;
   constexpr int LK = KD + 4, LC = C + 4;
   __shared__ float sG[C][KD + 1];
-  __shared__ float sKE[C * LK], sQE[C * LK], sKR[C * LK];
+  __shared__ __attribute__((aligned(16))) float sKE[C * LK];
+  __shared__ __attribute__((aligned(16))) float sQE[C * LK];
+  __shared__ __attribute__((aligned(16))) float sKR[C * LK];
   __shared__ float sA[C * LC];
   __shared__ float sBeta[C];
   __shared__ int sSlow;
@@ -119,9 +121,14 @@ prep_kernel(const float* __restrict__ q, const float* __restrict__ k, const floa
   if (tid < KD) {
     const int ch = tid;
     const float db = (dt_bias && ch < K) ? dt_bias[h * K + ch] : 0.0f;
+    // the 32 inputs first (independent loads), then the dependent sum
+    float zv[C];
+#pragma unroll
+    for (int t = 0; t < C; ++t) zv[t] = (t < nval && ch < K) ? z[(row0 + t) * K + ch] : 0.0f;
     float G = 0.0f;
+#pragma unroll
     for (int t = 0; t < C; ++t) {
-      if (t < nval && ch < K) G += gate_g(z[(row0 + t) * K + ch], db, gm);
+      if (t < nval && ch < K) G += gate_g(zv[t], db, gm);
       sG[t][ch] = G;
     }
     const float m = sG[15][ch];
@@ -136,23 +143,31 @@ prep_kernel(const float* __restrict__ q, const float* __restrict__ k, const floa
   if (tid == 0) rec[Rc::FLAG] = slow ? 1.0f : 0.0f;
   if (tid < C) rec[Rc::BETA + tid] = sBeta[tid];
   if (slow) return;                            // the token path needs nothing else
-  for (int i = tid; i < C * KD; i += 256) {
-    const int t = i / KD, ch = i % KD;
-    const float E = sG[t][ch] - sG[15][ch];
-    const float L = expn(E), Rr = expn(-E);
-    float kv = 0.0f, qv = 0.0f;
+  // four channels per thread and step: 16-byte loads and stores (K is a multiple of 4)
+  for (int i4 = tid; i4 < C * KD / 4; i4 += 256) {
+    const int i = 4 * i4, t = i / KD, ch = i % KD;
+    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
     if (t < nval && ch < K) {
-      kv = k[(row0 + t) * K + ch];
-      qv = q[(row0 + t) * K + ch];
+      kv = *reinterpret_cast<const float4*>(k + (row0 + t) * K + ch);
+      qv = *reinterpret_cast<const float4*>(q + (row0 + t) * K + ch);
     }
-    const float ke = kv * L, qe = scale * qv * L, kr = kv * Rr;
-    sKE[t * LK + ch] = ke;
-    sQE[t * LK + ch] = qe;
-    sKR[t * LK + ch] = kr;
-    rec[Rc::KE + i] = ke;
-    rec[Rc::QE + i] = qe;
-    rec[Rc::KR + i] = kr;
-    rec[Rc::E + i] = E;
+    float4 E, ke, qe, kr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float e = sG[t][ch + j] - sG[15][ch + j];
+      const float L = expn(e), Rr = expn(-e);
+      E[j] = e;
+      ke[j] = kv[j] * L;
+      qe[j] = scale * qv[j] * L;
+      kr[j] = kv[j] * Rr;
+    }
+    *reinterpret_cast<float4*>(sKE + t * LK + ch) = ke;
+    *reinterpret_cast<float4*>(sQE + t * LK + ch) = qe;
+    *reinterpret_cast<float4*>(sKR + t * LK + ch) = kr;
+    *reinterpret_cast<float4*>(rec + Rc::KE + i) = ke;
+    *reinterpret_cast<float4*>(rec + Rc::QE + i) = qe;
+    *reinterpret_cast<float4*>(rec + Rc::KR + i) = kr;
+    *reinterpret_cast<float4*>(rec + Rc::E + i) = E;
   }
   __syncthreads();
   // A (strictly lower) and P (lower) on MFMA: 2 x 2 tiles each, two tiles per wave

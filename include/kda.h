@@ -229,7 +229,7 @@ size_t kda_chunk_bwd_workspace_bytes(int B, int H, int T, int K, int V, int chun
  *   dg (B,H,T,K) w.r.t. the log-decay g;  dbeta (B,H,T);  dstate_in (B,H,K,V).
  * workspace: device buffer of at least kda_chunk_bwd_workspace_bytes(), 16-byte
  * aligned (KDA_ERR_ALIGN otherwise: the kernels read it in 16-byte vectors); its
- * contents on entry are ignored.  v and d_o must be 16-byte aligned, q, k, z 8-byte
+ * contents on entry are ignored.  q, k, v and d_o must be 16-byte aligned, z 8-byte
  * (KDA_ERR_ALIGN).  B * H <= 65535.  Currently dtype must be KDA_F32.  The blocks are
  * 32 tokens whatever `chunk` (16, 32 or 64) says; a block whose decay inside it is too
  * strong for the factorised form (beyond a factor exp(60) either side of its middle)

@@ -137,6 +137,8 @@ def test_argument_errors_before_launch():
     assert lib.kda_chunk_bwd(*args, P(g[0].value + 4), 1 << 40, 1, 1, 16, 8, 8, 0, None) == -8
     argv = [q, k, P(v.value + 8)] + args[3:]                   # v 8-byte but not 16-byte aligned
     assert lib.kda_chunk_bwd(*argv, g[0], 1 << 40, 1, 1, 16, 8, 8, 0, None) == -8
+    argq = [P(q.value + 8)] + args[1:]                          # q likewise
+    assert lib.kda_chunk_bwd(*argq, g[0], 1 << 40, 1, 1, 16, 8, 8, 0, None) == -8
     # gate adjoint: no output / null input, bad dtype, bad shape, workspace, aliasing
     ws = fake[11]
     assert lib.kda_gate_bwd(z, A, dt, g[0], None, None, None, ws, 1 << 20, 1, 1, 16, 8, 0, None) == -1
@@ -161,7 +163,7 @@ def test_argument_errors_before_launch():
     assert lib.kda_gate_bwd_noalloc(z, A, dt, g[0], o, None, None, 2, 1, 16384 * 128 + 1, 128, 0, None) == -10
     rej1 = (ctypes.c_ulonglong * 6)()
     lib.kda_get_counters(rej1, 6)
-    assert rej1[4] - rej0[4] == 41 and list(rej1[:4]) == list(rej0[:4]) and rej1[5] == rej0[5]
+    assert rej1[4] - rej0[4] == 42 and list(rej1[:4]) == list(rej0[:4]) and rej1[5] == rej0[5]
 
 
 @pytest.mark.skipif(_gpu_visible(), reason="fake device pointers: CPU-only check")

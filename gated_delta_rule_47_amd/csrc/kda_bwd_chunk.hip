@@ -27,7 +27,7 @@
 //   dg = the reverse cumulative sum of dG over the chunk's tokens          (gradient pass)
 // (m is held fixed: the rearrangement does not depend on it, so its own gradient is 0).
 //
-// Four kernels:
+// Four passes:
 //   prep     one workgroup per (head, chunk): the gate, E, KE, QE, KR, A and P on MFMA
 //            (v_mfma_f32_16x16x4_f32), T by substitution, G0, D0, beta, into the workspace;
 //   forward  one workgroup per (head, 16 value columns), chunks in order: the state at
@@ -36,11 +36,12 @@
 //            cotangents, dZ, dv and the initial state's gradient;
 //   gradient one workgroup per (head, chunk): every other gradient, from the chunk's
 //            checkpoint and chunk-end cotangent, all value columns at once (the sums over
-//            value columns stay in the workgroup: no partial buffers, no atomics).
+//            value columns stay in the workgroup: no partial buffers, no atomics); a
+//            second launch takes the token-path chunks.
 // A chunk whose decay inside it exceeds exp(+-60) around the reference (the factors
-// would leave fp32) is flagged by prep and evaluated token by token, exactly, by the same
-// kernels; the cotangent's path through a token does not involve the state, so only the
-// gradient kernel recomputes states (from the checkpoint, token by token).
+// would leave fp32) is flagged by prep and evaluated token by token, exactly; the
+// cotangent's path through a token does not involve the state, so only the gradient pass
+// recomputes states (from the checkpoint, token by token, in grad_token_kernel).
 #include "kda_common.h"
 #include "kda_launch.h"
 
@@ -265,28 +266,35 @@ __device__ __forceinline__ float4 load_rows16(const float* base, size_t row0, in
 // One workgroup per (head, 16 value columns), chunks in order.  The state tile lives in
 // LDS as [KD][16].
 template <int KD>
-__global__ void __launch_bounds__(256)
-fwd_kernel(const float* __restrict__ k, const float* __restrict__ v, const float* __restrict__ z,
-           const float* __restrict__ A_log, const float* __restrict__ dt_bias, const float* __restrict__ beta,
-           const float* __restrict__ state_in, char* __restrict__ ws, int H, int T, int K, int V, int VP, int nck) {
+constexpr int fwd_lds_floats() {
+  return KD * 16 + 2 * C * (KD + 4) + C * (C + 4) + 4 * C * 16 + 2 * KD + C + 4 + 256 + KD + 16;
+}
+
+template <int KD>
+__device__ __forceinline__ void fwd_pass(float* __restrict__ lds, int vt, int bh, int BH, const float* __restrict__ k,
+                                         const float* __restrict__ v, const float* __restrict__ z,
+                                         const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+                                         const float* __restrict__ beta, const float* __restrict__ state_in,
+                                         char* __restrict__ ws, int H, int T, int K, int V, int VP, int nck) {
   using Rc = Rec<KD>;
   constexpr int LK = KD + 4, LC = C + 4;
   constexpr int NK = C * KD / 4, NI = (NK + 255) / 256;
-  __shared__ __attribute__((aligned(16))) float sS[KD * 16];
-  __shared__ __attribute__((aligned(16))) float sKE[C * LK];
-  __shared__ __attribute__((aligned(16))) float sKR[C * LK];
-  __shared__ __attribute__((aligned(16))) float sT[C * LC];
-  __shared__ __attribute__((aligned(16))) float sZ[C * 16];
-  __shared__ __attribute__((aligned(16))) float sU[C * 16];
-  __shared__ __attribute__((aligned(16))) float sPart[2 * C * 16];
-  __shared__ __attribute__((aligned(16))) float sMisc[2 * KD + C + 4];   // G0, D0, beta, flag
-  __shared__ float sRed[256], sVec[KD], sE[16];
+  float* sS = lds;                             // [KD][16]
+  float* sKE = sS + KD * 16;
+  float* sKR = sKE + C * LK;
+  float* sT = sKR + C * LK;
+  float* sZ = sT + C * LC;
+  float* sU = sZ + C * 16;
+  float* sPart = sU + C * 16;
+  float* sMisc = sPart + 2 * C * 16;           // G0, D0, beta, flag
+  float* sRed = sMisc + 2 * KD + C + 4;
+  float* sVec = sRed + 256;
+  float* sE = sVec + KD;
   float* sG0 = sMisc;
   float* sD0 = sMisc + KD;
   float* sBeta = sMisc + 2 * KD;
-  const int vt = blockIdx.x, bh = blockIdx.y, h = bh % H, v0 = 16 * vt;
+  const int h = bh % H, v0 = 16 * vt;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const long long BH = (long long)gridDim.y;
   const Layout lo = layout(KD, VP, BH, nck);
   const float* recs = reinterpret_cast<const float*>(ws + lo.rec);
   float* ck = reinterpret_cast<float*>(ws + lo.ck);
@@ -413,31 +421,40 @@ fwd_kernel(const float* __restrict__ k, const float* __restrict__ v, const float
 // One workgroup per (head, 16 value columns), chunks in reverse; the cotangent tile dS
 // lives in LDS as [KD][16].
 template <int KD>
-__global__ void __launch_bounds__(256)
-rev_kernel(const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ z,
-           const float* __restrict__ A_log, const float* __restrict__ dt_bias, const float* __restrict__ beta,
-           float scale, const float* __restrict__ d_o, const float* __restrict__ d_state_out, char* __restrict__ ws,
-           float* __restrict__ dv, float* __restrict__ dstate_in, int H, int T, int K, int V, int VP, int nck) {
+constexpr int rev_lds_floats() {
+  return KD * 16 + 3 * C * (KD + 4) + 2 * C * (C + 4) + 3 * C * 16 + 2 * KD + C + 4 + 256 + 2 * KD + 16;
+}
+
+template <int KD>
+__device__ __forceinline__ void rev_pass(float* __restrict__ lds, int vt, int bh, int BH, const float* __restrict__ q,
+                                         const float* __restrict__ k, const float* __restrict__ z,
+                                         const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+                                         const float* __restrict__ beta, float scale, const float* __restrict__ d_o,
+                                         const float* __restrict__ d_state_out, char* __restrict__ ws,
+                                         float* __restrict__ dv, float* __restrict__ dstate_in, int H, int T, int K,
+                                         int V, int VP, int nck) {
   using Rc = Rec<KD>;
   constexpr int LK = KD + 4, LC = C + 4;
   constexpr int NK = C * KD / 4, NI = (NK + 255) / 256;
-  __shared__ __attribute__((aligned(16))) float sD[KD * 16];
-  __shared__ __attribute__((aligned(16))) float sQE[C * LK];
-  __shared__ __attribute__((aligned(16))) float sKE[C * LK];
-  __shared__ __attribute__((aligned(16))) float sKR[C * LK];
-  __shared__ __attribute__((aligned(16))) float sP[C * LC];
-  __shared__ __attribute__((aligned(16))) float sT[C * LC];
-  __shared__ __attribute__((aligned(16))) float sDO[C * 16];
-  __shared__ __attribute__((aligned(16))) float sDU[C * 16];
-  __shared__ __attribute__((aligned(16))) float sDZ[C * 16];
-  __shared__ __attribute__((aligned(16))) float sMisc[2 * KD + C + 4];   // G0, D0, beta, flag
-  __shared__ float sRed[256], sVec[KD], sAl[KD], sE[16];
+  float* sD = lds;                             // [KD][16]
+  float* sQE = sD + KD * 16;
+  float* sKE = sQE + C * LK;
+  float* sKR = sKE + C * LK;
+  float* sP = sKR + C * LK;
+  float* sT = sP + C * LC;
+  float* sDO = sT + C * LC;
+  float* sDU = sDO + C * 16;
+  float* sDZ = sDU + C * 16;
+  float* sMisc = sDZ + C * 16;                 // G0, D0, beta, flag
+  float* sRed = sMisc + 2 * KD + C + 4;
+  float* sVec = sRed + 256;
+  float* sAl = sVec + KD;
+  float* sE = sAl + KD;
   float* sG0 = sMisc;
   float* sD0 = sMisc + KD;
   float* sBeta = sMisc + 2 * KD;
-  const int vt = blockIdx.x, bh = blockIdx.y, h = bh % H, v0 = 16 * vt;
+  const int h = bh % H, v0 = 16 * vt;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const long long BH = (long long)gridDim.y;
   const Layout lo = layout(KD, VP, BH, nck);
   const float* recs = reinterpret_cast<const float*>(ws + lo.rec);
   float* dse = reinterpret_cast<float*>(ws + lo.dse);
@@ -571,40 +588,78 @@ rev_kernel(const float* __restrict__ q, const float* __restrict__ k, const float
   }
 }
 
+// The two sequential passes do not depend on each other (the reverse pass needs only the
+// prep records and d_o), so one launch runs both, 2 VP / 16 workgroups per head: slot
+// x < VP / 16 takes the forward pass of value tile x, the others the reverse pass of tile
+// x - VP / 16.  Their LDS is one shared buffer, so that a forward and a reverse workgroup
+// fit one CU together.  Every value tile of a pass reads the same chunk records; when the
+// head count is a multiple of 8, all workgroups of a head go to one XCD (workgroup i runs
+// on XCD i % 8), so that the records come from HBM once and from that XCD's L2 after.
+template <int KD>
+__global__ void __launch_bounds__(256)
+seq_kernel(const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+           const float* __restrict__ z, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+           const float* __restrict__ beta, const float* __restrict__ state_in, float scale,
+           const float* __restrict__ d_o, const float* __restrict__ d_state_out, char* __restrict__ ws,
+           float* __restrict__ dv, float* __restrict__ dstate_in, int H, int T, int K, int V, int VP, int nck,
+           int BH) {
+  __shared__ __attribute__((aligned(16))) float lds[cmax(fwd_lds_floats<KD>(), rev_lds_floats<KD>())];
+  const int nt = VP / 16, per = 2 * nt;
+  const int i = blockIdx.x;
+  int bh, x;
+  if ((BH & 7) == 0) {
+    const int r = i >> 3;                      // rank within XCD i % 8
+    bh = (i & 7) + 8 * (r / per);
+    x = r % per;
+  } else {
+    bh = i / per;
+    x = i % per;
+  }
+  if (x < nt)
+    fwd_pass<KD>(lds, x, bh, BH, k, v, z, A_log, dt_bias, beta, state_in, ws, H, T, K, V, VP, nck);
+  else
+    rev_pass<KD>(lds, x - nt, bh, BH, q, k, z, A_log, dt_bias, beta, scale, d_o, d_state_out, ws, dv, dstate_in, H,
+                 T, K, V, VP, nck);
+}
+
 // ============================================================================ gradient
 // One workgroup (8 waves) per (head, chunk), all value columns.  The products over the
-// value columns go in slabs of 32 columns through LDS.
+// value columns go in slabs of 32 columns through LDS.  The slab buffers and the chunk's
+// KE, QE, KR are not needed at the same time and share one LDS region (66 KB in all at
+// KD = 128), so two workgroups fit one CU and each hides the other's load latency.
+// Chunks on the token path are left to grad_token_kernel.
 template <int KD>
 struct GradCfg {
   static constexpr int LK = KD + 4, LC = C + 4, LS = 32 + 4;
   static constexpr int NCT = KD / 16;                 // channel tiles
   static constexpr int NTT = 2 * NCT;                 // [token][channel] output tiles
   static constexpr int NTW = (NTT + 7) / 8;           // of them per wave
-  // fast path LDS (floats)
-  static constexpr int F_KE = 0, F_QE = F_KE + C * LK, F_KR = F_QE + C * LK;
-  static constexpr int F_A = F_KR + C * LK, F_DP = F_A + C * LC, F_DA = F_DP + C * LC;
-  static constexpr int F_DO = F_DA + C * LC, F_DZ = F_DO + C * LS, F_U = F_DZ + C * LS;
-  static constexpr int F_ST = F_U + C * LS, F_DX = F_ST + KD * LS;
-  static constexpr int F_DG = F_ST, F_KW = F_ST + C * LK;   // after the slab loop (over S~, dX)
-  static constexpr int F_END = cmax(F_DX + KD * LS, F_KW + C * LK);
-  static constexpr int F_MISC = F_END;                      // beta, G0, D0, dbeta, rowsum(dX S~)
+  static constexpr int NCH = (KD * 8 + 511) / 512;    // float4 of a state slab per thread
+  // region X, first the slab (dO, dZ, U over tokens; S~, dX over channels), then KE, QE,
+  // KR; at the end dG and KW overwrite KE and QE in place
+  static constexpr int X_DO = 0, X_DZ = X_DO + C * LS, X_U = X_DZ + C * LS;
+  static constexpr int X_ST = X_U + C * LS, X_DX = X_ST + KD * LS;
+  static constexpr int X_KE = 0, X_QE = C * LK, X_KR = 2 * C * LK;
+  static constexpr int X_END = cmax(X_DX + KD * LS, 3 * C * LK);
+  static constexpr int F_A = X_END, F_DP = F_A + C * LC, F_DA = F_DP + C * LC;
+  static constexpr int F_MISC = F_DA + C * LC;        // beta, G0, D0, dbeta, rowsum(dX S~)
   static constexpr int F_TOTAL = F_MISC + C + 2 * KD + C + KD;
 };
 
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void st4(float* p, float4 x) { *reinterpret_cast<float4*>(p) = x; }
+__device__ __forceinline__ float dot4(float4 a, float4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
+
 template <int KD, int VP>
-__global__ void __launch_bounds__(512)
-grad_kernel(const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-            const float* __restrict__ z, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
-            const float* __restrict__ beta, float scale, const float* __restrict__ d_o, const char* __restrict__ ws,
-            float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dg, float* __restrict__ dbeta, int H,
-            int T, int K, int V, int nck) {
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4)))
+grad_kernel(const float* __restrict__ d_o, const char* __restrict__ ws, float scale, float* __restrict__ dq,
+            float* __restrict__ dk, float* __restrict__ dg, float* __restrict__ dbeta, int T, int K, int V,
+            int nck) {
   using Rc = Rec<KD>;
   using G = GradCfg<KD>;
-  constexpr int LK = G::LK, LC = G::LC, LS = G::LS;
-  constexpr int SLOW_F = 2 * KD * VP + 4 * KD + 4 * VP + 512 + 4;
-  constexpr int SMEM = cmax(G::F_TOTAL, SLOW_F);
-  __shared__ __attribute__((aligned(16))) float sm[SMEM];
-  const int c = blockIdx.x, bh = blockIdx.y, h = bh % H;
+  constexpr int LK = G::LK, LC = G::LC, LS = G::LS, NCH = G::NCH;
+  __shared__ __attribute__((aligned(16))) float sm[G::F_TOTAL];
+  const int c = blockIdx.x, bh = blockIdx.y;
   const int t0 = c * C, nval = min(C, T - t0);
   const size_t row0 = (size_t)bh * T + t0;
   const size_t chunk = (size_t)bh * nck + c;
@@ -616,190 +671,265 @@ grad_kernel(const float* __restrict__ q, const float* __restrict__ k, const floa
   const float* up = reinterpret_cast<const float*>(ws + lo.u) + chunk * C * VP;
   const float* yp = reinterpret_cast<const float*>(ws + lo.y) + chunk * C * VP;
   const float* dzp = reinterpret_cast<const float*>(ws + lo.dz) + chunk * C * VP;
-  const bool slow = rec[Rc::FLAG] != 0.0f;
+  if (rec[Rc::FLAG] != 0.0f) return;           // the token path's chunk
 
-  if (!slow) {
-    float* sKE = sm + G::F_KE;
-    float* sQE = sm + G::F_QE;
-    float* sKR = sm + G::F_KR;
-    float* sA = sm + G::F_A;
-    float* sDP = sm + G::F_DP;
-    float* sDA = sm + G::F_DA;
-    float* sDO = sm + G::F_DO;
-    float* sDZ = sm + G::F_DZ;
-    float* sU = sm + G::F_U;
-    float* sST = sm + G::F_ST;
-    float* sDX = sm + G::F_DX;
-    float* sBeta = sm + G::F_MISC;
-    float* sG0 = sBeta + C;
-    float* sD0 = sG0 + KD;
-    float* sDB = sD0 + KD;
-    float* sXS = sDB + C;
-    for (int i = tid; i < C * KD; i += 512) {
-      const int t = i / KD, ch = i % KD;
-      sKE[t * LK + ch] = rec[Rc::KE + i];
-      sQE[t * LK + ch] = rec[Rc::QE + i];
-      sKR[t * LK + ch] = rec[Rc::KR + i];
+  float* sDO = sm + G::X_DO;
+  float* sDZ = sm + G::X_DZ;
+  float* sU = sm + G::X_U;
+  float* sST = sm + G::X_ST;
+  float* sDX = sm + G::X_DX;
+  float* sKE = sm + G::X_KE;
+  float* sQE = sm + G::X_QE;
+  float* sKR = sm + G::X_KR;
+  float* sA = sm + G::F_A;
+  float* sDP = sm + G::F_DP;
+  float* sDA = sm + G::F_DA;
+  float* sBeta = sm + G::F_MISC;
+  float* sG0 = sBeta + C;
+  float* sD0 = sG0 + KD;
+  float* sDB = sD0 + KD;
+  float* sXS = sDB + C;
+  for (int i = tid; i < C * C / 4; i += 512) {
+    const int r = (4 * i) / C, col = (4 * i) % C;
+    st4(sA + r * LC + col, ld4(rec + Rc::A + 4 * i));
+  }
+  for (int i = tid; i < KD; i += 512) {
+    sG0[i] = rec[Rc::G0 + i];
+    sD0[i] = rec[Rc::D0 + i];
+  }
+  if (tid < C) {
+    sBeta[tid] = rec[Rc::BETA + tid];
+    sDB[tid] = 0.0f;
+  }
+  // slab operands in registers: token rows (threads 0..255: token tid / 8, columns
+  // 4 (tid % 8) .. +3) and channel rows (float4 i = tid + 512 m: channel i / 8)
+  const int st_t = tid >> 3, st_f = tid & 7;
+  float4 rDO, rDZ, rU, rY, rCK[NCH], rDS[NCH];
+  auto load_slab = [&](int v0) __attribute__((always_inline)) {
+    if (tid < 256) {
+      const size_t g = (size_t)st_t * VP + v0 + 4 * st_f;
+      const bool ok = st_t < nval && v0 + 4 * st_f < V;
+      rDO = ok ? ld4(d_o + (row0 + st_t) * V + v0 + 4 * st_f) : make_float4(0.f, 0.f, 0.f, 0.f);
+      rDZ = ld4(dzp + g);
+      rU = ld4(up + g);
+      rY = ld4(yp + g);
     }
-    for (int i = tid; i < C * C; i += 512) sA[(i / C) * LC + i % C] = rec[Rc::A + i];
-    for (int i = tid; i < KD; i += 512) {
-      sG0[i] = rec[Rc::G0 + i];
-      sD0[i] = rec[Rc::D0 + i];
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+      const int i = tid + 512 * m;
+      if (i < KD * 8) {
+        const size_t off = (size_t)(i >> 3) * VP + v0 + 4 * (i & 7);
+        rCK[m] = ld4(ckp + off);
+        rDS[m] = ld4(dsep + off);
+      }
     }
-    if (tid < C) {
-      sBeta[tid] = rec[Rc::BETA + tid];
-      sDB[tid] = 0.0f;
+  };
+  // accumulators: dQE, dKE and W = U dX^T on [token][channel] tiles wave + 8 i; dP (waves
+  // 0..3) or dM (waves 4..7) on one [token][token] tile
+  floatx4 aQ[G::NTW], aK[G::NTW], aW[G::NTW], aPM = zero4();
+#pragma unroll
+  for (int i = 0; i < G::NTW; ++i) aQ[i] = aK[i] = aW[i] = zero4();
+  // elementwise sums: rowsum(dX S~) of the thread's channels, sum_v dZ Y of its token
+  float xs[NCH], zy = 0.0f;
+#pragma unroll
+  for (int m = 0; m < NCH; ++m) xs[m] = 0.0f;
+  __syncthreads();                             // sBeta, sG0, sD0
+#pragma unroll 1
+  for (int v0 = 0; v0 < VP; v0 += 32) {
+    if (v0) __syncthreads();                   // (the previous slab is consumed)
+    load_slab(v0);
+    if (tid < 256) {
+      st4(sDO + st_t * LS + 4 * st_f, rDO);
+      st4(sDZ + st_t * LS + 4 * st_f, rDZ);
+      st4(sU + st_t * LS + 4 * st_f, rU);
+      zy += dot4(rDZ, rY);
     }
-    // accumulators: dQE, dKE and W = U dX^T on [token][channel] tiles wave + 8 i; dP (waves
-    // 0..3) or dM (waves 4..7) on one [token][token] tile
-    floatx4 aQ[G::NTW], aK[G::NTW], aW[G::NTW], aPM = zero4();
 #pragma unroll
-    for (int i = 0; i < G::NTW; ++i) aQ[i] = aK[i] = aW[i] = zero4();
-    // elementwise sums: rowsum(dX S~) of channel tid / TPC over the thread's columns, and
-    // sum_v dZ Y of token tid / 16
-    constexpr int TPC = 512 / KD;                      // threads per channel
-    float xs = 0.0f, zy = 0.0f;
-    for (int v0 = 0; v0 < VP; v0 += 32) {
-      __syncthreads();                                 // (the previous slab is consumed)
-      {
-        const int t = tid >> 4;                        // token tid / 16, columns tid % 16 (+ 16)
-        for (int j = tid & 15; j < 32; j += 16) {
-          const size_t g = (size_t)t * VP + v0 + j;
-          const bool ok = t < nval && v0 + j < V;
-          sDO[t * LS + j] = ok ? d_o[(row0 + t) * V + v0 + j] : 0.0f;
-          const float dzv = dzp[g];
-          sDZ[t * LS + j] = dzv;
-          sU[t * LS + j] = up[g];
-          zy = fmaf(dzv, yp[g], zy);
-        }
-      }
-      {
-        const int ch = tid / TPC;                      // channel tid / TPC, every TPC-th column
-        for (int j = tid % TPC; j < 32; j += TPC) {
-          const float st = sG0[ch] * ckp[ch * VP + v0 + j];
-          const float dx = sD0[ch] * dsep[ch * VP + v0 + j];
-          sST[ch * LS + j] = st;
-          sDX[ch * LS + j] = dx;
-          xs = fmaf(st, dx, xs);
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < G::NTW; ++i) {
-        const int tau = wave + 8 * i;
-        if (tau < G::NTT) {
-          const int rt = tau / G::NCT, ct = tau % G::NCT;
-          const int ti = 16 * rt + (lane & 15), ci = 16 * ct + (lane & 15);
-          const float nb = -sBeta[ti];
-#pragma unroll
-          for (int d = 0; d < 32; d += 4) {
-            const int dd = d + (lane >> 4);
-            const float st = sST[ci * LS + dd];
-            aQ[i] = mma(sDO[ti * LS + dd], st, aQ[i]);
-            aK[i] = mma(nb * sDZ[ti * LS + dd], st, aK[i]);
-            aW[i] = mma(sU[ti * LS + dd], sDX[ci * LS + dd], aW[i]);
-          }
-        }
-      }
-      {
-        const int ti = 16 * ((wave >> 1) & 1) + (lane & 15), tj = 16 * (wave & 1) + (lane & 15);
-        const float* pa = wave < 4 ? sDO : sDZ;
-        const float sg = wave < 4 ? 1.0f : -1.0f;
-#pragma unroll
-        for (int d = 0; d < 32; d += 4) {
-          const int dd = d + (lane >> 4);
-          aPM = mma(sg * pa[ti * LS + dd], sU[tj * LS + dd], aPM);
-        }
+    for (int m = 0; m < NCH; ++m) {
+      const int i = tid + 512 * m;
+      if (i < KD * 8) {
+        const int ch = i >> 3, j = 4 * (i & 7);
+        const float g0 = sG0[ch], d0 = sD0[ch];
+        const float4 st = make_float4(g0 * rCK[m].x, g0 * rCK[m].y, g0 * rCK[m].z, g0 * rCK[m].w);
+        const float4 dx = make_float4(d0 * rDS[m].x, d0 * rDS[m].y, d0 * rDS[m].z, d0 * rDS[m].w);
+        st4(sST + ch * LS + j, st);
+        st4(sDX + ch * LS + j, dx);
+        xs[m] += dot4(st, dx);
       }
     }
     __syncthreads();
-    // dP (lower) and dA = diag(beta) dM (strictly lower) to LDS; dbeta gets sum_j dM_tj A_tj
-    {
-      const int ti0 = 16 * ((wave >> 1) & 1), tj0 = 16 * (wave & 1);
-      float rs[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = ti0 + 4 * (lane >> 4) + r, j = tj0 + (lane & 15);
-        if (wave < 4) {
-          sDP[i * LC + j] = j <= i ? aPM[r] : 0.0f;
-          rs[r] = 0.0f;
-        } else {
-          const float dm = j < i ? aPM[r] : 0.0f;
-          sDA[i * LC + j] = sBeta[i] * dm;
-          rs[r] = dm * sA[i * LC + j];
-        }
-      }
-      if (wave >= 4) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = rs[r];
-          x += __shfl_xor(x, 1);
-          x += __shfl_xor(x, 2);
-          x += __shfl_xor(x, 4);
-          x += __shfl_xor(x, 8);
-          if ((lane & 15) == 0) atomicAdd(&sDB[ti0 + 4 * (lane >> 4) + r], x);
-        }
-      }
-    }
-    // the per-thread sums: rowsum(dX S~) per channel, sum_v dZ Y per token
-    for (int m = 1; m < TPC; m <<= 1) xs += __shfl_xor(xs, m);
-    for (int m = 1; m < 16; m <<= 1) zy += __shfl_xor(zy, m);
-    __syncthreads();                           // dP, dA complete; S~ and dX no longer read
-    float* sDG = sm + G::F_DG;
-    float* sKW = sm + G::F_KW;
-    if (tid % TPC == 0) sXS[tid / TPC] = xs;
-    if ((tid & 15) == 0 && (tid >> 4) < C) atomicAdd(&sDB[tid >> 4], zy);
-    // second products (depth: the chunk's tokens), then the elementwise gradients
-    const float* Erec = rec + Rc::E;
 #pragma unroll
     for (int i = 0; i < G::NTW; ++i) {
       const int tau = wave + 8 * i;
       if (tau < G::NTT) {
         const int rt = tau / G::NCT, ct = tau % G::NCT;
         const int ti = 16 * rt + (lane & 15), ci = 16 * ct + (lane & 15);
-        floatx4 aR = aW[i];
-#pragma unroll
-        for (int d = 0; d < C; d += 4) {
+        const float nb = -sBeta[ti];
+#pragma unroll 2
+        for (int d = 0; d < 32; d += 4) {
           const int dd = d + (lane >> 4);
-          const float kr = sKR[dd * LK + ci];
-          aQ[i] = mma(sDP[ti * LC + dd], kr, aQ[i]);
-          aK[i] = mma(sDA[ti * LC + dd], kr, aK[i]);
-          aR = mma(sDP[dd * LC + ti], sQE[dd * LK + ci], aR);
-          aR = mma(sDA[dd * LC + ti], sKE[dd * LK + ci], aR);
+          const float st = sST[ci * LS + dd];
+          aQ[i] = mma(sDO[ti * LS + dd], st, aQ[i]);
+          aK[i] = mma(nb * sDZ[ti * LS + dd], st, aK[i]);
+          aW[i] = mma(sU[ti * LS + dd], sDX[ci * LS + dd], aW[i]);
         }
+      }
+    }
+    {
+      const int ti = 16 * ((wave >> 1) & 1) + (lane & 15), tj = 16 * (wave & 1) + (lane & 15);
+      const float* pa = wave < 4 ? sDO : sDZ;
+      const float sg = wave < 4 ? 1.0f : -1.0f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * rt + 4 * (lane >> 4) + r, ch = 16 * ct + (lane & 15);
-          const float ke = sKE[t * LK + ch], qe = sQE[t * LK + ch], kr = sKR[t * LK + ch];
-          const float E = Erec[t * KD + ch];
-          const float L = expn(E), Rr = expn(-E);
-          sDG[t * LK + ch] = aK[i][r] * ke + aQ[i][r] * qe - aR[r] * kr;
-          sKW[t * LK + ch] = kr * aW[i][r];
-          if (t < nval && ch < K) {
-            dk[(row0 + t) * K + ch] = aK[i][r] * L + aR[r] * Rr;
-            dq[(row0 + t) * K + ch] = scale * aQ[i][r] * L;
-          }
+      for (int d = 0; d < 32; d += 4) {
+        const int dd = d + (lane >> 4);
+        aPM = mma(sg * pa[ti * LS + dd], sU[tj * LS + dd], aPM);
+      }
+    }
+  }
+  // dP (lower) and dA = diag(beta) dM (strictly lower) to LDS; dbeta gets sum_j dM_tj A_tj
+  {
+    const int ti0 = 16 * ((wave >> 1) & 1), tj0 = 16 * (wave & 1);
+    float rs[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = ti0 + 4 * (lane >> 4) + r, j = tj0 + (lane & 15);
+      if (wave < 4) {
+        sDP[i * LC + j] = j <= i ? aPM[r] : 0.0f;
+        rs[r] = 0.0f;
+      } else {
+        const float dm = j < i ? aPM[r] : 0.0f;
+        sDA[i * LC + j] = sBeta[i] * dm;
+        rs[r] = dm * sA[i * LC + j];
+      }
+    }
+    if (wave >= 4) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = rs[r];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        x += __shfl_xor(x, 8);
+        if ((lane & 15) == 0) atomicAdd(&sDB[ti0 + 4 * (lane >> 4) + r], x);
+      }
+    }
+  }
+  // the per-thread sums: rowsum(dX S~) per channel (8 threads a channel), sum_v dZ Y per
+  // token (8 threads a token)
+#pragma unroll
+  for (int m = 0; m < NCH; ++m) {
+    xs[m] += __shfl_xor(xs[m], 1);
+    xs[m] += __shfl_xor(xs[m], 2);
+    xs[m] += __shfl_xor(xs[m], 4);
+  }
+  zy += __shfl_xor(zy, 1);
+  zy += __shfl_xor(zy, 2);
+  zy += __shfl_xor(zy, 4);
+  __syncthreads();                             // the slab region is free; dP, dA complete
+#pragma unroll
+  for (int m = 0; m < NCH; ++m) {
+    const int i = tid + 512 * m;
+    if (i < KD * 8 && (i & 7) == 0) sXS[i >> 3] = xs[m];
+  }
+  if (tid < 256 && st_f == 0) atomicAdd(&sDB[st_t], zy);
+  for (int i = tid; i < C * KD / 4; i += 512) {
+    const int t = (4 * i) / KD, ch = (4 * i) % KD;
+    st4(sKE + t * LK + ch, ld4(rec + Rc::KE + 4 * i));
+    st4(sQE + t * LK + ch, ld4(rec + Rc::QE + 4 * i));
+    st4(sKR + t * LK + ch, ld4(rec + Rc::KR + 4 * i));
+  }
+  // E of the thread's output elements (for L and R), ahead of the products
+  const float* Erec = rec + Rc::E;
+  float rE[G::NTW][4];
+#pragma unroll
+  for (int i = 0; i < G::NTW; ++i) {
+    const int tau = wave + 8 * i;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      rE[i][r] = 0.0f;
+      if (tau < G::NTT) {
+        const int t = 16 * (tau / G::NCT) + 4 * (lane >> 4) + r, ch = 16 * (tau % G::NCT) + (lane & 15);
+        rE[i][r] = Erec[t * KD + ch];
+      }
+    }
+  }
+  __syncthreads();
+  // second products (depth: the chunk's tokens)
+  floatx4 aR[G::NTW];
+#pragma unroll
+  for (int i = 0; i < G::NTW; ++i) {
+    const int tau = wave + 8 * i;
+    aR[i] = aW[i];
+    if (tau < G::NTT) {
+      const int rt = tau / G::NCT, ct = tau % G::NCT;
+      const int ti = 16 * rt + (lane & 15), ci = 16 * ct + (lane & 15);
+#pragma unroll
+      for (int d = 0; d < C; d += 4) {
+        const int dd = d + (lane >> 4);
+        const float kr = sKR[dd * LK + ci];
+        aQ[i] = mma(sDP[ti * LC + dd], kr, aQ[i]);
+        aK[i] = mma(sDA[ti * LC + dd], kr, aK[i]);
+        aR[i] = mma(sDP[dd * LC + ti], sQE[dd * LK + ci], aR[i]);
+        aR[i] = mma(sDA[dd * LC + ti], sKE[dd * LK + ci], aR[i]);
+      }
+    }
+  }
+  __syncthreads();                             // every wave is done reading KE, QE, KR
+  // the elementwise gradients; dG and KW = KR (U dX^T) replace KE and QE element by element
+  float* sDG = sKE;
+  float* sKW = sQE;
+#pragma unroll
+  for (int i = 0; i < G::NTW; ++i) {
+    const int tau = wave + 8 * i;
+    if (tau < G::NTT) {
+      const int rt = tau / G::NCT, ct = tau % G::NCT;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * rt + 4 * (lane >> 4) + r, ch = 16 * ct + (lane & 15);
+        const float ke = sKE[t * LK + ch], qe = sQE[t * LK + ch], kr = sKR[t * LK + ch];
+        const float L = expn(rE[i][r]), Rr = expn(-rE[i][r]);
+        sDG[t * LK + ch] = aK[i][r] * ke + aQ[i][r] * qe - aR[i][r] * kr;
+        sKW[t * LK + ch] = kr * aW[i][r];
+        if (t < nval && ch < K) {
+          dk[(row0 + t) * K + ch] = aK[i][r] * L + aR[i][r] * Rr;
+          dq[(row0 + t) * K + ch] = scale * aQ[i][r] * L;
         }
       }
     }
-    __syncthreads();
-    // dg: reverse cumulative sum over the chunk's tokens, from the chunk-end term
-    if (tid < KD) {
-      const int ch = tid;
-      float run = sXS[ch];
-      for (int t = 0; t < C; ++t) run += sKW[t * LK + ch];
-      for (int t = nval - 1; t >= 0; --t) {
-        run += sDG[t * LK + ch];
-        if (ch < K) dg[(row0 + t) * K + ch] = run;
-      }
-    }
-    if (tid < nval) dbeta[row0 + tid] = sDB[tid];
-    return;
   }
+  __syncthreads();
+  // dg: reverse cumulative sum over the chunk's tokens, from the chunk-end term
+  if (tid < KD) {
+    const int ch = tid;
+    float run = sXS[ch];
+    for (int t = 0; t < C; ++t) run += sKW[t * LK + ch];
+    for (int t = nval - 1; t >= 0; --t) {
+      run += sDG[t * LK + ch];
+      if (ch < K) dg[(row0 + t) * K + ch] = run;
+    }
+  }
+  if (tid < nval) dbeta[row0 + tid] = sDB[tid];
+}
 
-  // ---------------------------------------------------------------- token path
-  // Exact token-by-token reverse of the chunk from its checkpoint S_c and chunk-end
-  // cotangent: for t = last .. first, the states S_{t-1}, S_t are recomputed from S_c.
+// The gradients of a token-path chunk: an exact token-by-token reverse from the chunk's
+// checkpoint S_c and chunk-end cotangent, for t = last .. first, with the states S_{t-1},
+// S_t recomputed from S_c.  One workgroup per (head, group of GTOK chunks) takes the
+// group's flagged chunks in turn, so that the launch costs little when none is flagged.
+constexpr int GTOK = 16;
+
+template <int KD, int VP>
+__global__ void __launch_bounds__(512)
+grad_token_kernel(const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+                  const float* __restrict__ z, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+                  const float* __restrict__ beta, float scale, const float* __restrict__ d_o,
+                  const char* __restrict__ ws, float* __restrict__ dq, float* __restrict__ dk,
+                  float* __restrict__ dg, float* __restrict__ dbeta, int H, int T, int K, int V, int nck) {
+  using Rc = Rec<KD>;
+  constexpr int SMEM = 2 * KD * VP + 4 * KD + 4 * VP + 512 + 4;
+  __shared__ __attribute__((aligned(16))) float sm[SMEM];
+  const int bh = blockIdx.y, h = bh % H;
+  const int tid = threadIdx.x;
+  const Layout lo = layout(KD, VP, (long long)gridDim.y, nck);
   float* sS = sm;                               // [KD][VP]: S_{t-1}
   float* sD = sS + KD * VP;                     // [KD][VP]: dS
   float* sAl = sD + KD * VP;                    // alpha_t
@@ -811,129 +941,140 @@ grad_kernel(const float* __restrict__ q, const float* __restrict__ k, const floa
   float* sEv = sDo + VP;                        // e (v_t - S'^T k_t)
   float* sDe = sEv + VP;                        // de
   float* sPc = sDe + VP;                        // column-sum partials [512 / VP][VP]
-  float* sBt = sPc + 512;                      // beta_t
+  float* sBt = sPc + 512;                       // beta_t
   const float gm = gate_multiplier(A_log[h]);
   constexpr int RG = 512 / VP;                  // row groups of the column sums
   constexpr int TPC = 512 / KD;                 // threads per channel of the row sums
-  auto load_token = [&](int t) {
-    if (tid < KD) {
-      const int ch = tid;
-      const float db = (dt_bias && ch < K) ? dt_bias[h * K + ch] : 0.0f;
-      sAl[ch] = ch < K ? expn(gate_g(z[(row0 + t) * K + ch], db, gm)) : 0.0f;
-      sK[ch] = ch < K ? k[(row0 + t) * K + ch] : 0.0f;
-      sQ[ch] = ch < K ? scale * q[(row0 + t) * K + ch] : 0.0f;
-    }
-    if (tid < VP) {
-      sVv[tid] = tid < V ? v[(row0 + t) * V + tid] : 0.0f;
-      sDo[tid] = tid < V ? d_o[(row0 + t) * V + tid] : 0.0f;
-    }
-    if (tid == 0) sBt[0] = beta[row0 + t];
-    __syncthreads();
-  };
-  // out[col] = sum over rows of w[row] * f(row, col) for f = mat[row][col] * rowscale[row]
-  auto colsum = [&](const float* mat, const float* rscale, float* out) {
-    const int col = tid % VP, rg = tid / VP;
-    float s = 0.0f;
-    for (int r = rg; r < KD; r += RG) s = fmaf(mat[r * VP + col] * rscale[r], sK[r], s);
-    sPc[rg * VP + col] = s;
-    __syncthreads();
-    if (tid < VP) {
-      float a = 0.0f;
-      for (int g = 0; g < RG; ++g) a += sPc[g * VP + tid];
-      out[tid] = a;
-    }
-    __syncthreads();
-  };
-  // one token forward on sS with the loaded token: S' = alpha S, e = v - S'^T k, S = S' + beta k e^T
-  auto token_fwd = [&]() {
-    colsum(sS, sAl, sEv);
-    const float bt = sBt[0];
-    for (int i = tid; i < KD * VP; i += 512) {
-      const int r = i / VP, col = i % VP;
-      sS[i] = fmaf(sK[r], bt * (sVv[col] - sEv[col]), sAl[r] * sS[i]);
-    }
-    __syncthreads();
-  };
-  for (int i = tid; i < KD * VP; i += 512) sD[i] = dsep[i];
-  for (int t = nval - 1; t >= 0; --t) {
-    for (int i = tid; i < KD * VP; i += 512) sS[i] = ckp[i];
-    __syncthreads();
-    for (int u = 0; u < t; ++u) {
-      load_token(u);
-      token_fwd();
-    }
-    load_token(t);                               // sS = S_{t-1}
-    colsum(sS, sAl, sEv);                        // S'^T k
-    const float bt = sBt[0];
-    if (tid < VP) sEv[tid] = sVv[tid] - sEv[tid];   // e
-    __syncthreads();
-    // dS += q_hat do^T
-    for (int i = tid; i < KD * VP; i += 512) sD[i] = fmaf(sQ[i / VP], sDo[i % VP], sD[i]);
-    __syncthreads();
-    // row sums over the columns: dq = S_t do, dSe = dS e; thread (row tid / TPC, part tid % TPC)
-    {
-      const int r = tid / TPC, p = tid % TPC;
-      float aq = 0.0f, ae = 0.0f;
-      for (int col = p; col < VP; col += TPC) {
-        const float st = fmaf(sK[r], bt * sEv[col], sAl[r] * sS[r * VP + col]);
-        aq = fmaf(st, sDo[col], aq);
-        ae = fmaf(sD[r * VP + col], sEv[col], ae);
+  const int cend = min(nck, (int)(blockIdx.x + 1) * GTOK);
+  for (int c = blockIdx.x * GTOK; c < cend; ++c) {
+    const size_t chunk = (size_t)bh * nck + c;
+    const float* rec = reinterpret_cast<const float*>(ws + lo.rec) + chunk * Rc::SIZE;
+    if (rec[Rc::FLAG] == 0.0f) continue;       // (uniform over the workgroup)
+    const float* ckp = reinterpret_cast<const float*>(ws + lo.ck) + chunk * KD * VP;
+    const float* dsep = reinterpret_cast<const float*>(ws + lo.dse) + chunk * KD * VP;
+    const int t0 = c * C, nval = min(C, T - t0);
+    const size_t row0 = (size_t)bh * T + t0;
+    auto load_token = [&](int t) {
+      if (tid < KD) {
+        const int ch = tid;
+        const float db = (dt_bias && ch < K) ? dt_bias[h * K + ch] : 0.0f;
+        sAl[ch] = ch < K ? expn(gate_g(z[(row0 + t) * K + ch], db, gm)) : 0.0f;
+        sK[ch] = ch < K ? k[(row0 + t) * K + ch] : 0.0f;
+        sQ[ch] = ch < K ? scale * q[(row0 + t) * K + ch] : 0.0f;
       }
-      for (int m = 1; m < TPC; m <<= 1) {
-        aq += __shfl_xor(aq, m);
-        ae += __shfl_xor(ae, m);
+      if (tid < VP) {
+        sVv[tid] = tid < V ? v[(row0 + t) * V + tid] : 0.0f;
+        sDo[tid] = tid < V ? d_o[(row0 + t) * V + tid] : 0.0f;
       }
-      if (p == 0) {
-        if (r < K) dq[(row0 + t) * K + r] = scale * aq;
-        sX[r] = ae;                              // dS e
-      }
-    }
-    __syncthreads();
-    // de = beta dS^T k
-    {
+      if (tid == 0) sBt[0] = beta[row0 + t];
+      __syncthreads();
+    };
+    // out[col] = sum over rows of w[row] * f(row, col) for f = mat[row][col] * rowscale[row]
+    auto colsum = [&](const float* mat, const float* rscale, float* out) {
       const int col = tid % VP, rg = tid / VP;
       float s = 0.0f;
-      for (int r = rg; r < KD; r += RG) s = fmaf(sD[r * VP + col], sK[r], s);
+      for (int r = rg; r < KD; r += RG) s = fmaf(mat[r * VP + col] * rscale[r], sK[r], s);
       sPc[rg * VP + col] = s;
       __syncthreads();
       if (tid < VP) {
         float a = 0.0f;
         for (int g = 0; g < RG; ++g) a += sPc[g * VP + tid];
-        sDe[tid] = bt * a;
+        out[tid] = a;
+      }
+      __syncthreads();
+    };
+    // one token forward on sS with the loaded token: S' = alpha S, e = v - S'^T k, S = S' + beta k e^T
+    auto token_fwd = [&]() {
+      colsum(sS, sAl, sEv);
+      const float bt = sBt[0];
+      for (int i = tid; i < KD * VP; i += 512) {
+        const int r = i / VP, col = i % VP;
+        sS[i] = fmaf(sK[r], bt * (sVv[col] - sEv[col]), sAl[r] * sS[i]);
+      }
+      __syncthreads();
+    };
+    __syncthreads();                            // (the previous chunk is done with sD)
+    for (int i = tid; i < KD * VP; i += 512) sD[i] = dsep[i];
+    for (int t = nval - 1; t >= 0; --t) {
+      for (int i = tid; i < KD * VP; i += 512) sS[i] = ckp[i];
+      __syncthreads();
+      for (int u = 0; u < t; ++u) {
+        load_token(u);
+        token_fwd();
+      }
+      load_token(t);                               // sS = S_{t-1}
+      colsum(sS, sAl, sEv);                        // S'^T k
+      const float bt = sBt[0];
+      if (tid < VP) sEv[tid] = sVv[tid] - sEv[tid];   // e
+      __syncthreads();
+      // dS += q_hat do^T
+      for (int i = tid; i < KD * VP; i += 512) sD[i] = fmaf(sQ[i / VP], sDo[i % VP], sD[i]);
+      __syncthreads();
+      // row sums over the columns: dq = S_t do, dSe = dS e; thread (row tid / TPC, part tid % TPC)
+      {
+        const int r = tid / TPC, p = tid % TPC;
+        float aq = 0.0f, ae = 0.0f;
+        for (int col = p; col < VP; col += TPC) {
+          const float st = fmaf(sK[r], bt * sEv[col], sAl[r] * sS[r * VP + col]);
+          aq = fmaf(st, sDo[col], aq);
+          ae = fmaf(sD[r * VP + col], sEv[col], ae);
+        }
+        for (int m = 1; m < TPC; m <<= 1) {
+          aq += __shfl_xor(aq, m);
+          ae += __shfl_xor(ae, m);
+        }
+        if (p == 0) {
+          if (r < K) dq[(row0 + t) * K + r] = scale * aq;
+          sX[r] = ae;                              // dS e
+        }
+      }
+      __syncthreads();
+      // de = beta dS^T k
+      {
+        const int col = tid % VP, rg = tid / VP;
+        float s = 0.0f;
+        for (int r = rg; r < KD; r += RG) s = fmaf(sD[r * VP + col], sK[r], s);
+        sPc[rg * VP + col] = s;
+        __syncthreads();
+        if (tid < VP) {
+          float a = 0.0f;
+          for (int g = 0; g < RG; ++g) a += sPc[g * VP + tid];
+          sDe[tid] = bt * a;
+        }
+        __syncthreads();
+      }
+      // dbeta = k . dS e; dk = beta dS e - S' de; dS'' = dS - k de^T; dg = alpha rowsum(dS'' S_{t-1})
+      {
+        const int r = tid / TPC, p = tid % TPC;
+        float a1 = 0.0f, a2 = 0.0f;
+        for (int col = p; col < VP; col += TPC) {
+          const float sp = sAl[r] * sS[r * VP + col];
+          a1 = fmaf(sp, sDe[col], a1);
+          const float d2 = fmaf(-sK[r], sDe[col], sD[r * VP + col]);
+          a2 = fmaf(d2, sS[r * VP + col], a2);
+        }
+        for (int m = 1; m < TPC; m <<= 1) {
+          a1 += __shfl_xor(a1, m);
+          a2 += __shfl_xor(a2, m);
+        }
+        if (p == 0 && r < K) {
+          dk[(row0 + t) * K + r] = bt * sX[r] - a1;
+          dg[(row0 + t) * K + r] = sAl[r] * a2;
+        }
+      }
+      if (tid < 64) {
+        float x = 0.0f;
+        for (int r = tid; r < KD; r += 64) x = fmaf(sK[r], sX[r], x);
+        for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
+        if (tid == 0) dbeta[row0 + t] = x;
+      }
+      __syncthreads();
+      for (int i = tid; i < KD * VP; i += 512) {
+        const int r = i / VP, col = i % VP;
+        sD[i] = sAl[r] * fmaf(-sK[r], sDe[col], sD[i]);
       }
       __syncthreads();
     }
-    // dbeta = k . dS e; dk = beta dS e - S' de; dS'' = dS - k de^T; dg = alpha rowsum(dS'' S_{t-1})
-    {
-      const int r = tid / TPC, p = tid % TPC;
-      float a1 = 0.0f, a2 = 0.0f;
-      for (int col = p; col < VP; col += TPC) {
-        const float sp = sAl[r] * sS[r * VP + col];
-        a1 = fmaf(sp, sDe[col], a1);
-        const float d2 = fmaf(-sK[r], sDe[col], sD[r * VP + col]);
-        a2 = fmaf(d2, sS[r * VP + col], a2);
-      }
-      for (int m = 1; m < TPC; m <<= 1) {
-        a1 += __shfl_xor(a1, m);
-        a2 += __shfl_xor(a2, m);
-      }
-      if (p == 0 && r < K) {
-        dk[(row0 + t) * K + r] = bt * sX[r] - a1;
-        dg[(row0 + t) * K + r] = sAl[r] * a2;
-      }
-    }
-    if (tid < 64) {
-      float x = 0.0f;
-      for (int r = tid; r < KD; r += 64) x = fmaf(sK[r], sX[r], x);
-      for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
-      if (tid == 0) dbeta[row0 + t] = x;
-    }
-    __syncthreads();
-    for (int i = tid; i < KD * VP; i += 512) {
-      const int r = i / VP, col = i % VP;
-      sD[i] = sAl[r] * fmaf(-sK[r], sDe[col], sD[i]);
-    }
-    __syncthreads();
   }
 }
 
@@ -951,16 +1092,16 @@ static hipError_t launch_kd_vp(const float* q, const float* k, const float* v, c
     hipLaunchKernelGGL(prep_kernel<KD>, dim3(nck, BH), dim3(256), 0, s, q, k, z, A_log, dt_bias, beta, scale,
                        reinterpret_cast<float*>(ws + lo.rec), H, T, K, nck);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(fwd_kernel<KD>, dim3(VP / 16, BH), dim3(256), 0, s, k, v, z, A_log, dt_bias, beta, state_in,
-                       ws, H, T, K, V, VP, nck);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(rev_kernel<KD>, dim3(VP / 16, BH), dim3(256), 0, s, q, k, z, A_log, dt_bias, beta, scale, d_o,
-                     d_state_out, ws, dv, dstate_in, H, T, K, V, VP, nck);
+  hipLaunchKernelGGL(seq_kernel<KD>, dim3(2 * (VP / 16) * BH), dim3(256), 0, s, q, k, v, z, A_log, dt_bias, beta,
+                     state_in, scale, d_o, d_state_out, ws, dv, dstate_in, H, T, K, V, VP, nck, BH);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (T > 0) {
-    hipLaunchKernelGGL((grad_kernel<KD, VP>), dim3(nck, BH), dim3(512), 0, s, q, k, v, z, A_log, dt_bias, beta, scale,
-                       d_o, ws, dq, dk, dg, dbeta, H, T, K, V, nck);
+    hipLaunchKernelGGL((grad_kernel<KD, VP>), dim3(nck, BH), dim3(512), 0, s, d_o, ws, scale, dq, dk, dg, dbeta, T,
+                       K, V, nck);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((grad_token_kernel<KD, VP>), dim3((nck + GTOK - 1) / GTOK, BH), dim3(512), 0, s, q, k, v, z,
+                       A_log, dt_bias, beta, scale, d_o, ws, dq, dk, dg, dbeta, H, T, K, V, nck);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

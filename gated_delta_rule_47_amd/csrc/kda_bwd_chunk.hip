@@ -422,7 +422,7 @@ __device__ __forceinline__ void fwd_pass(float* __restrict__ lds, int vt, int bh
 // lives in LDS as [KD][16].
 template <int KD>
 constexpr int rev_lds_floats() {
-  return KD * 16 + 3 * C * (KD + 4) + 2 * C * (C + 4) + 3 * C * 16 + 2 * KD + C + 4 + 256 + 2 * KD + 16;
+  return KD * 16 + 3 * C * (KD + 4) + 2 * C * (C + 4) + 4 * C * 16 + 2 * KD + C + 4 + 256 + 2 * KD + 16;
 }
 
 template <int KD>
@@ -443,8 +443,8 @@ __device__ __forceinline__ void rev_pass(float* __restrict__ lds, int vt, int bh
   float* sP = sKR + C * LK;
   float* sT = sP + C * LC;
   float* sDO = sT + C * LC;
-  float* sDU = sDO + C * 16;
-  float* sDZ = sDU + C * 16;
+  float* sDU = sDO + C * 16;                   // two partial sums [2][C][16]
+  float* sDZ = sDU + 2 * C * 16;
   float* sMisc = sDZ + C * 16;                 // G0, D0, beta, flag
   float* sRed = sMisc + 2 * KD + C + 4;
   float* sVec = sRed + 256;
@@ -505,18 +505,26 @@ __device__ __forceinline__ void rev_pass(float* __restrict__ lds, int vt, int bh
     if (!slow) {
       for (int i = tid; i < KD * 16; i += 256) sD[i] *= sD0[i >> 4];   // dX = diag(D0) dS
       __syncthreads();
-      // dU = P^T dO + KR dX
-      if (wave < 2) {
-        const int rt = wave;
+      // dU = P^T dO + KR dX in two partial sums over all four waves: row tile wave & 1;
+      // part 0 takes P^T dO and KR dX over the channels [0, D1), part 1 the rest
+      {
+        constexpr int D1 = KD > 32 ? (KD - 32) / 2 : 0;
+        const int rt = wave & 1, part = wave >> 1;
         floatx4 acc = zero4();
+        if (part == 0) {
 #pragma unroll
-        for (int d = 0; d < C; d += 4)
-          acc = mma(sP[(d + (lane >> 4)) * LC + 16 * rt + (lane & 15)], sDO[(d + (lane >> 4)) * 16 + (lane & 15)], acc);
-#pragma unroll 8
-        for (int d = 0; d < KD; d += 4)
-          acc = mma(sKR[(16 * rt + (lane & 15)) * LK + d + (lane >> 4)], sD[(d + (lane >> 4)) * 16 + (lane & 15)], acc);
+          for (int d = 0; d < C; d += 4)
+            acc = mma(sP[(d + (lane >> 4)) * LC + 16 * rt + (lane & 15)], sDO[(d + (lane >> 4)) * 16 + (lane & 15)], acc);
+#pragma unroll 4
+          for (int d = 0; d < D1; d += 4)
+            acc = mma(sKR[(16 * rt + (lane & 15)) * LK + d + (lane >> 4)], sD[(d + (lane >> 4)) * 16 + (lane & 15)], acc);
+        } else {
+#pragma unroll 4
+          for (int d = D1; d < KD; d += 4)
+            acc = mma(sKR[(16 * rt + (lane & 15)) * LK + d + (lane >> 4)], sD[(d + (lane >> 4)) * 16 + (lane & 15)], acc);
+        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sDU[(16 * rt + 4 * (lane >> 4) + r) * 16 + (lane & 15)] = acc[r];
+        for (int r = 0; r < 4; ++r) sDU[part * C * 16 + (16 * rt + 4 * (lane >> 4) + r) * 16 + (lane & 15)] = acc[r];
       }
       __syncthreads();
       // dZ = T^T dU; dv = diag(beta) dZ
@@ -524,8 +532,10 @@ __device__ __forceinline__ void rev_pass(float* __restrict__ lds, int vt, int bh
         const int rt = wave;
         floatx4 acc = zero4();
 #pragma unroll
-        for (int d = 0; d < C; d += 4)
-          acc = mma(sT[(d + (lane >> 4)) * LC + 16 * rt + (lane & 15)], sDU[(d + (lane >> 4)) * 16 + (lane & 15)], acc);
+        for (int d = 0; d < C; d += 4) {
+          const int e = (d + (lane >> 4)) * 16 + (lane & 15);
+          acc = mma(sT[(d + (lane >> 4)) * LC + 16 * rt + (lane & 15)], sDU[e] + sDU[C * 16 + e], acc);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * rt + 4 * (lane >> 4) + r, j = lane & 15;

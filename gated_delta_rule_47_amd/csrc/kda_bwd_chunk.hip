@@ -712,10 +712,12 @@ grad_kernel(const float* __restrict__ d_o, const char* __restrict__ ws, float sc
     sDB[tid] = 0.0f;
   }
   // slab operands in registers: token rows (threads 0..255: token tid / 8, columns
-  // 4 (tid % 8) .. +3) and channel rows (float4 i = tid + 512 m: channel i / 8)
+  // 4 (tid % 8) .. +3) and channel rows (float4 i = tid + 512 m: channel i / 8).  The
+  // channel rows (the bulk: S~ and dX) of the next slab are loaded while the current one
+  // is multiplied; the token rows are loaded when they are needed.
   const int st_t = tid >> 3, st_f = tid & 7;
   float4 rDO, rDZ, rU, rY, rCK[NCH], rDS[NCH];
-  auto load_slab = [&](int v0) __attribute__((always_inline)) {
+  auto load_tok = [&](int v0) __attribute__((always_inline)) {
     if (tid < 256) {
       const size_t g = (size_t)st_t * VP + v0 + 4 * st_f;
       const bool ok = st_t < nval && v0 + 4 * st_f < V;
@@ -724,6 +726,8 @@ grad_kernel(const float* __restrict__ d_o, const char* __restrict__ ws, float sc
       rU = ld4(up + g);
       rY = ld4(yp + g);
     }
+  };
+  auto load_ch = [&](int v0) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < NCH; ++m) {
       const int i = tid + 512 * m;
@@ -743,11 +747,12 @@ grad_kernel(const float* __restrict__ d_o, const char* __restrict__ ws, float sc
   float xs[NCH], zy = 0.0f;
 #pragma unroll
   for (int m = 0; m < NCH; ++m) xs[m] = 0.0f;
+  load_ch(0);
   __syncthreads();                             // sBeta, sG0, sD0
 #pragma unroll 1
   for (int v0 = 0; v0 < VP; v0 += 32) {
     if (v0) __syncthreads();                   // (the previous slab is consumed)
-    load_slab(v0);
+    load_tok(v0);
     if (tid < 256) {
       st4(sDO + st_t * LS + 4 * st_f, rDO);
       st4(sDZ + st_t * LS + 4 * st_f, rDZ);
@@ -767,6 +772,7 @@ grad_kernel(const float* __restrict__ d_o, const char* __restrict__ ws, float sc
         xs[m] += dot4(st, dx);
       }
     }
+    if (v0 + 32 < VP) load_ch(v0 + 32);       // in flight during this slab's products
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < G::NTW; ++i) {

@@ -456,7 +456,9 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     const int pos = g;                          // quarter of the half: tokens 16*half + tq .. +3
     const int tq = 4 * pos;
     const bool kact = KD == 128 || 2 * pair < K;  // (K = KD = 128: every pair is a channel pair)
-    const bool precise = gmul > 64.0f;
+    // the precise softplus for strong gates (its small values matter once multiplied) and
+    // for a zero multiplier (softplus2_direct can be +inf)
+    const bool precise = !(gmul > 0.0f) || gmul > 64.0f;
     // dt_bias in log2 units: the gate is taken as -gmul softplus2(z log2(e) + dt_bias log2(e))
     const float dtb0 = (kact && dt_bias) ? dt_bias[SG ? h : h * K + 2 * pair] * kLog2e : 0.0f;
     const float dtb1 = (kact && dt_bias) ? dt_bias[SG ? h : h * K + 2 * pair + 1] * kLog2e : 0.0f;
@@ -542,9 +544,10 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       float ax = 0.0f, ay = 0.0f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        ax = fmaf(-gmul, softplus2_f(fmaf(rz[t].x(), kLog2e, dtb0), PRECISE), ax);
+        const float spx = fmaf(rz[t].x(), kLog2e, dtb0), spy = fmaf(rz[t].y(), kLog2e, dtb1);
+        ax = fmaf(-gmul, PRECISE ? softplus2_f(spx, true) : softplus2_direct(spx), ax);
         if constexpr (SG) ay = ax;             // one gate per token: both channels share it
-        else ay = fmaf(-gmul, softplus2_f(fmaf(rz[t].y(), kLog2e, dtb1), PRECISE), ay);
+        else ay = fmaf(-gmul, PRECISE ? softplus2_f(spy, true) : softplus2_direct(spy), ay);
         px[t] = ax;
         py[t] = ay;
       }

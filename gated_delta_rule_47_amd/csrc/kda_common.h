@@ -72,6 +72,12 @@ __device__ __forceinline__ float softplus2_f(float x2, bool precise) {
   return fmaxf(x2, 0.0f) + l;
 }
 
+// log2(1 + 2^x2) evaluated directly: two transcendentals and one add.  Within fp32 rounding
+// of softplus2_f for x2 < 128; from there on it is +inf.  A caller that multiplies it by a
+// positive gate multiplier then sees a -inf decay, which sends the block to its exact
+// token path; with a zero multiplier it would make a NaN, so such heads use softplus2_f.
+__device__ __forceinline__ float softplus2_direct(float x2) { return fast_log2(1.0f + fast_exp2(x2)); }
+
 // ------------------------------------------------------------------ MFMA fragments
 // One wave computes a 16x16 fp32 tile C += A(16 x KS) * B(KS x 16) per instruction.
 // Operands live in LDS "depth-contiguous": A as [row][depth], B as [col][depth].

@@ -446,6 +446,29 @@ def test_k128_saturated_gates_and_many_heads():
     _check("state", Sg, S_ref, TOL["bf16"])
 
 
+def test_k128_gate_inputs_beyond_the_direct_softplus_range():
+    """The fused kernel takes softplus as log2(1 + 2^x) directly, which is +inf from
+    x = z log2(e) >= 128 (z >= ~89): such a block must take the exact token path and still
+    match, even where the true decay is mild (A_log = -10, so -g stays tiny), while z = 80
+    (2^115, finite) stays on the factorised path."""
+    wl = ks.WORKLOADS["nano"].with_(B=1, H=3, K=128, V=128, chunk=64, a_log="list:-10,0,-3", state="normal:0.1")
+    x = ks.generate(wl, T=100)
+    x["z"][0, 0, 5] = 120.0                     # mild head: only the +inf sends this block to the token path
+    x["z"][0, 0, 40:44] = 80.0
+    x["z"][0, 1, 70, :64] = 100.0               # half of the channels of one token
+    x["z"][0, 2, 33] = 80.0
+    x["z"] = ks.round_bf16(x["z"])
+    d = upload(wl, x)
+    o, S = _fwd(d, 64)
+    heads = [(0, 0), (0, 1), (0, 2)]
+    o_ref, S_ref = oracle_heads(wl, x, heads)
+    og = np.stack([host(o[b, h]) for b, h in heads])[None]
+    Sg = np.stack([host(S[b, h]) for b, h in heads])[None]
+    assert np.isfinite(og).all() and np.isfinite(Sg).all()
+    _check("o", og, o_ref, TOL["bf16"])
+    _check("state", Sg, S_ref, TOL["bf16"])
+
+
 def test_k128_state_none_and_in_place_state():
     wl = ks.WORKLOADS["nano"].with_(B=1, H=4, K=128, V=128, chunk=64, state="normal:0.1")
     x = ks.generate(wl, T=97)

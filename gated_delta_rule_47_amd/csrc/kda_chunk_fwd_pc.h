@@ -370,6 +370,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   constexpr int CD = Cfg::CD, NB = Cfg::NB, NNT = Cfg::NNT, NMT = Cfg::NMT;
   constexpr int LD_TK = Cfg::LD_TK, LD_CT = Cfg::LD_CT, LD_A = Cfg::LD_A;
   constexpr int NS = KD / 32;                         // 32-deep channel slices
+  // E waves split each channel pair between two waves when KD <= 64 (per-channel gate)
+  constexpr bool PSPLIT = KD <= 64 && !SG;
   constexpr int NTHR = Cfg::NWAVES * 64;
 
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
@@ -449,9 +451,13 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     // channels 32*(e % 4) .. +31.  The block's decay reference sits between its two
     // halves, so a half needs nothing from the other one: the first half's exponents
     // are minus the decay still to come before the reference, the second half's are
-    // the decay since it.
+    // the decay since it.  With KD <= 64 (per-channel gate) the waves that would hold
+    // no channels take half of the others' instead: waves 2j and 2j + 1 of a half share
+    // the 32 channels of group j, each the even or the odd channel of every pair (par),
+    // so that each E wave does half the work of the KD = 128 mapping.
     const int half = wave >> 2;
-    const int cw = wave & 3;
+    const int cw = PSPLIT ? (wave & 3) >> 1 : wave & 3;
+    const int par = PSPLIT ? wave & 1 : 0;     // the lane's channel of its pair (PSPLIT)
     const int pair = 16 * cw + l16;            // key-channel pair
     const int pos = g;                          // quarter of the half: tokens 16*half + tq .. +3
     const int tq = 4 * pos;
@@ -460,7 +466,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     // for a zero multiplier (softplus2_direct can be +inf)
     const bool precise = !(gmul > 0.0f) || gmul > 64.0f;
     // dt_bias in log2 units: the gate is taken as -gmul softplus2(z log2(e) + dt_bias log2(e))
-    const float dtb0 = (kact && dt_bias) ? dt_bias[SG ? h : h * K + 2 * pair] * kLog2e : 0.0f;
+    // (PSPLIT: dtb0 is the lane's own channel)
+    const float dtb0 = (kact && dt_bias) ? dt_bias[SG ? h : h * K + 2 * pair + par] * kLog2e : 0.0f;
     const float dtb1 = (kact && dt_bias) ? dt_bias[SG ? h : h * K + 2 * pair + 1] * kLog2e : 0.0f;
     // per-head buffer resources: offsets past the head's T tokens read as 0
     const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(k + tb * K, (unsigned)(T * K * 2));
@@ -488,7 +495,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     const unsigned vbase = (kact && 16 * half < C) ? (unsigned)((16 * half + tq) * rowb + 4 * pair) : 0x80000000u;
     // SG: byte offset of the lane's first gate value (one bf16 per token) in block 0
     const unsigned zbase = (kact && 16 * half < C) ? (unsigned)((16 * half + tq) * 2) : 0x80000000u;
-    const int dpoff = kact ? 8 * pair : 0;     // this lane's channel pair in a per-channel fp32 array
+    // this lane's channel pair (PSPLIT: its channel) in a per-channel fp32 array, bytes
+    const int dpoff = kact ? (PSPLIT ? 4 * (2 * pair + par) : 8 * pair) : 0;
     // element offset of the lane's first token row and channel pair in a [token][channel] tile
     const int rowoff = (16 * half + tq) * LD_TK + perm32(2 * pair);
     auto load_qkz = [&](int b, Raw& r) __attribute__((always_inline)) {
@@ -612,6 +620,97 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       lds_wait_asm();                          // the asm writes above, before the barrier
     };
 
+    // The same for a PSPLIT wave: one channel (2 pair + par) of the lane's pair, so one
+    // gate, one scan and two exponentials per token; the bf16 results of tokens t and
+    // t + 2 are packed into one register and stored as two 16-bit halves.
+    auto e1p = [&](auto precise_tag, auto half_tag, int b, int sl, int slp, const Raw& cur)
+                   __attribute__((always_inline)) {
+      constexpr bool PRECISE = decltype(precise_tag)::value;
+      constexpr int HALF = decltype(half_tag)::value;
+      const int tn = b * C;
+      const int nval = min(C, T - tn);
+      char* sb = set_at(sl);
+      bf16_t* sKE = reinterpret_cast<bf16_t*>(sb + Cfg::SET_KE);
+      bf16_t* sQE = reinterpret_cast<bf16_t*>(sb + Cfg::SET_QE);
+      bf16_t* sKR = reinterpret_cast<bf16_t*>(sb + Cfg::SET_KR);
+      float* sG0 = reinterpret_cast<float*>(sb + Cfg::SET_G0);
+      float* sD0 = reinterpret_cast<float*>(sb + Cfg::SET_D0);
+      // the lane's bf16 of a pair word as fp32 bits (a byte permute: the low or the high
+      // half into the high half, zeros below)
+      const unsigned sel = par ? 0x03020c0cu : 0x01000c0cu;
+      auto own = [&](uint32_t w) __attribute__((always_inline)) {
+        return __uint_as_float(__builtin_amdgcn_perm(w, w, sel));
+      };
+      float zv[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) zv[t] = own(cur.z[t]);
+      float dprev = 0.0f;
+      if constexpr (HALF == 0) dprev = *reinterpret_cast<const float*>(set_at(slp) + Cfg::SET_D0 + dpoff);
+      if (nval < 16 * HALF + 16) {             // identity tokens: gate 0
+        const int lim = nval - (16 * HALF + tq);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) zv[t] = t < lim ? zv[t] : -INFINITY;
+      }
+      float px[4];
+      float ax = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float sp = fmaf(zv[t], kLog2e, dtb0);
+        ax = fmaf(-gmul, PRECISE ? softplus2_f(sp, true) : softplus2_direct(sp), ax);
+        px[t] = ax;
+      }
+      float sumx, exx;
+      quarter_scan(ax, g, sumx, exx);
+      const float offx = HALF == 0 ? exx - sumx : exx;
+      float g0 = 0.0f, fp = 0.0f;
+      if constexpr (HALF == 0) {
+        g0 = fast_exp2(sumx);
+        fp = dprev * g0;
+      }
+      const unsigned long long bal = __ballot(kact && sumx < -thresh);
+      if (lane == 0) sFlag[sl * Cfg::NE + wave] = bal != 0ull;
+      const int c = 2 * pair + par;
+      if (HALF == 0 && kact && g == 0) {
+        sG0[c] = g0;
+        if (b > 0) *reinterpret_cast<float*>(set_at(slp) + Cfg::SET_F + 4 * c) = fp;
+      }
+      if (kact) {
+        float l3 = 0.0f;
+        uint32_t wke[2], wqe[2], wkr[2];       // tokens t (low half) and t + 2 (high half)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float ke[2], qe[2], kr[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int tt = t + 2 * u;
+            const float ex = px[tt] + offx;
+            const float L = fast_exp2(ex), Rr = fast_exp2(-ex);
+            const float kv = own(cur.k[tt]), qv = own(cur.q[tt]);
+            ke[u] = -kv * L;                   // KE is stored negated (see e1)
+            qe[u] = qv * L;
+            kr[u] = kv * Rr;
+            if (tt == 3) l3 = L;
+          }
+          wke[t] = pack_bf16x2(ke[0], ke[1]);
+          wqe[t] = pack_bf16x2(qe[0], qe[1]);
+          wkr[t] = pack_bf16x2(kr[0], kr[1]);
+        }
+        auto put2 = [&](bf16_t* tile, const uint32_t* w) __attribute__((always_inline)) {
+          unsigned short* e = reinterpret_cast<unsigned short*>(tile + rowoff + par);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            e[t * LD_TK] = (unsigned short)w[t];
+            e[(t + 2) * LD_TK] = (unsigned short)(w[t] >> 16);
+          }
+        };
+        put2(sKE, wke);
+        put2(sQE, wqe);
+        put2(sKR, wkr);
+        // D0 = 2^(G_last - m): the second half's last token, whose L it is
+        if (HALF == 1 && g == 3) sD0[c] = l3;
+      }
+    };
+
     Raw ra, rb, rc;
     load_qkz(0, ra);                           // (blocks past the end read zeros)
     load_qkz(1, rb);
@@ -625,7 +724,15 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       if (b < nck) {
         using H0 = std::integral_constant<int, 0>;
         using H1 = std::integral_constant<int, 1>;
-        if (precise) {
+        if constexpr (PSPLIT) {
+          if (precise) {
+            if (half) e1p(std::true_type{}, H1{}, b, sl, slp, cur);
+            else e1p(std::true_type{}, H0{}, b, sl, slp, cur);
+          } else {
+            if (half) e1p(std::false_type{}, H1{}, b, sl, slp, cur);
+            else e1p(std::false_type{}, H0{}, b, sl, slp, cur);
+          }
+        } else if (precise) {
           if (half) e1(std::true_type{}, H1{}, b, sl, slp, cur, nxt);
           else e1(std::true_type{}, H0{}, b, sl, slp, cur, nxt);
         } else {

@@ -107,6 +107,8 @@ prep_kernel(const float* __restrict__ q, const float* __restrict__ k, const floa
   __shared__ __attribute__((aligned(16))) float sQE[C * LK];
   __shared__ __attribute__((aligned(16))) float sKR[C * LK];
   __shared__ float sA[C * LC];
+  __shared__ float sT[C * LC];
+  __shared__ float sX[16 * 16];
   __shared__ float sBeta[C];
   __shared__ int sSlow;
   const int c = blockIdx.x, bh = blockIdx.y, h = bh % H;
@@ -115,6 +117,19 @@ prep_kernel(const float* __restrict__ q, const float* __restrict__ k, const floa
   float* rec = recs + ((size_t)bh * nck + c) * Rc::SIZE;
   const float gm = gate_multiplier(A_log[h]);
   const size_t row0 = (size_t)bh * T + t0;
+  // k and q of the element pass, loaded first so that they arrive during the gate's sum:
+  // four channels per thread and float4 i4 = tid + 256 m (K is a multiple of 4)
+  constexpr int NI = (C * KD / 4 + 255) / 256;
+  float4 kv[NI], qv[NI];
+#pragma unroll
+  for (int m = 0; m < NI; ++m) {
+    const int i4 = tid + 256 * m, t = (4 * i4) / KD, ch = (4 * i4) % KD;
+    kv[m] = qv[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i4 < C * KD / 4 && t < nval && ch < K) {
+      kv[m] = *reinterpret_cast<const float4*>(k + (row0 + t) * K + ch);
+      qv[m] = *reinterpret_cast<const float4*>(q + (row0 + t) * K + ch);
+    }
+  }
   if (tid == 0) sSlow = 0;
   if (tid < C) sBeta[tid] = tid < nval ? beta[row0 + tid] : 0.0f;
   __syncthreads();
@@ -144,23 +159,21 @@ prep_kernel(const float* __restrict__ q, const float* __restrict__ k, const floa
   if (tid == 0) rec[Rc::FLAG] = slow ? 1.0f : 0.0f;
   if (tid < C) rec[Rc::BETA + tid] = sBeta[tid];
   if (slow) return;                            // the token path needs nothing else
-  // four channels per thread and step: 16-byte loads and stores (K is a multiple of 4)
-  for (int i4 = tid; i4 < C * KD / 4; i4 += 256) {
+  // four channels per thread and step: 16-byte stores
+#pragma unroll
+  for (int m = 0; m < NI; ++m) {
+    const int i4 = tid + 256 * m;
+    if (i4 >= C * KD / 4) break;
     const int i = 4 * i4, t = i / KD, ch = i % KD;
-    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
-    if (t < nval && ch < K) {
-      kv = *reinterpret_cast<const float4*>(k + (row0 + t) * K + ch);
-      qv = *reinterpret_cast<const float4*>(q + (row0 + t) * K + ch);
-    }
     float4 E, ke, qe, kr;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float e = sG[t][ch + j] - sG[15][ch + j];
       const float L = expn(e), Rr = expn(-e);
       E[j] = e;
-      ke[j] = kv[j] * L;
-      qe[j] = scale * qv[j] * L;
-      kr[j] = kv[j] * Rr;
+      ke[j] = kv[m][j] * L;
+      qe[j] = scale * qv[m][j] * L;
+      kr[j] = kv[m][j] * Rr;
     }
     *reinterpret_cast<float4*>(sKE + t * LK + ch) = ke;
     *reinterpret_cast<float4*>(sQE + t * LK + ch) = qe;
@@ -190,22 +203,47 @@ prep_kernel(const float* __restrict__ q, const float* __restrict__ k, const floa
     }
   }
   __syncthreads();
-  // T = (I + diag(beta) A)^-1 by forward substitution: lane l holds column l
-  if (wave == 0) {
-    float x[C];
+  // T = M^-1 for M = I + diag(beta) A, in 16-row blocks: M = [[M00, 0], [M10, M11]] gives
+  // T00 = M00^-1 and T11 = M11^-1 by forward substitution (waves 0 and 1 side by side, lane
+  // l < 16 holding column l: T_il = delta_il - beta_i sum_{j<i} A_ij T_jl), then
+  // T10 = -T11 (M10 T00) from two 16 x 16 products; T01 = 0.
+  if (wave < 2 && lane < 16) {
+    const int I = wave;
+    float x[16];
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-      float s = i == lane ? 1.0f : 0.0f;
-      const float bi = sBeta[i];
+    for (int i = 0; i < 16; ++i) {
+      const int r = 16 * I + i;
+      const float bi = sBeta[r];
+      float s0 = i == lane ? 1.0f : 0.0f, s1 = 0.0f;
 #pragma unroll
-      for (int j = 0; j < i; ++j) s = fmaf(-bi * sA[i * LC + j], x[j], s);
-      x[i] = s;
+      for (int j = 0; j < i; ++j) {
+        const float a = -bi * sA[r * LC + 16 * I + j];
+        if (j & 1) s1 = fmaf(a, x[j], s1);
+        else s0 = fmaf(a, x[j], s0);
+      }
+      x[i] = s0 + s1;
     }
-    if (lane < C) {
 #pragma unroll
-      for (int i = 0; i < C; ++i) rec[Rc::T + i * C + lane] = x[i];
-    }
+    for (int i = 0; i < 16; ++i) sT[(16 * I + i) * LC + 16 * I + lane] = x[i];
   }
+  __syncthreads();
+  const int ti = tid >> 4, tj = tid & 15;      // one element of a 16 x 16 block per thread
+  {
+    float s = 0.0f;
+#pragma unroll
+    for (int l = 0; l < 16; ++l) s = fmaf(sA[(16 + ti) * LC + l], sT[l * LC + tj], s);
+    sX[ti * 16 + tj] = sBeta[16 + ti] * s;     // M10 T00
+  }
+  __syncthreads();
+  {
+    float s = 0.0f;
+#pragma unroll
+    for (int l = 0; l < 16; ++l) s = fmaf(sT[(16 + ti) * LC + 16 + l], sX[l * 16 + tj], s);
+    sT[(16 + ti) * LC + tj] = -s;
+    sT[ti * LC + 16 + tj] = 0.0f;
+  }
+  __syncthreads();
+  for (int e = tid; e < C * C; e += 256) rec[Rc::T + e] = sT[(e / C) * LC + e % C];
 }
 
 // Column sums over the KD rows of a [KD][16] LDS tile weighted by w[KD]: 256 threads, thread

@@ -7,7 +7,8 @@
 //                    operands KE, QE, KR (V reads KR^T from KR with transposing LDS
 //                    reads); wave e covers one 16-token half of
 //                    the block and 32 key channels, from q, k, z loaded straight into
-//                    registers two blocks ahead;
+//                    registers two blocks ahead (KD <= 64: two waves share a channel
+//                    group, each taking the even or the odd channel of every pair);
 //   V (waves 8-11):  the state-dependent part, each wave owning 16 value columns and all
 //                    K rows of the fp32 state in accumulator registers: with
 //                    S~ = diag(G0) S,  Y = V - KE S~,  U = (I + A)^-1 diag(beta) Y,

@@ -74,6 +74,7 @@ struct PcCfg {
   static constexpr int NNT = VD / 16;                 // value-column tiles = active V waves
   static constexpr int NMT = KD / 16;                 // key-row tiles of the state
   static constexpr int NE = 8, NV = 4, NW = 4;        // waves of the E, V and W stages
+  static_assert(NE == 8, "the slow flags of a block are read as one 8-byte word");
   static constexpr int NWAVES = NE + NV + NW;
   // Row strides of the bf16 operand tiles, in elements.  Within each 32-wide slice of a
   // row, the contraction index is stored in the order of perm32(), so that an MFMA operand
@@ -116,7 +117,7 @@ struct PcCfg {
   static constexpr int OFF_WS = OFF_A + CD * LD_A * 4;
   static constexpr int OFF_VRAW = OFF_WS + 2 * WS_BYTES;
   static constexpr int OFF_FLAG = OFF_VRAW + 3 * VRAW_BUF;
-  static constexpr int TOTAL = OFF_FLAG + 3 * NE * 4;
+  static constexpr int TOTAL = OFF_FLAG + 3 * NE;     // slow flags: one byte per E wave and block slot
   static_assert(TOTAL <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
   static_assert(KD % 32 == 0 && KD <= 128 && (C == 16 || C == 32) && NNT <= NV, "tile shape");
   static_assert(SET_BYTES % 16 == 0 && WO_BYTES % 16 == 0 && OFF_A % 16 == 0 && OFF_WS % 16 == 0 && OFF_VRAW % 16 == 0 &&
@@ -378,7 +379,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   __shared__ __attribute__((aligned(16))) u32x2 s_pw[NORM ? Pn::PW_WORDS : 1];
   float* sA = reinterpret_cast<float*>(smem + Cfg::OFF_A);
-  int* sFlag = reinterpret_cast<int*>(smem + Cfg::OFF_FLAG);   // [block % 3][E wave]
+  unsigned char* sFlag = reinterpret_cast<unsigned char*>(smem + Cfg::OFF_FLAG);   // [block % 3][E wave]
   // Buffer offsets of block b, passed through an empty asm so that the compiler keeps them
   // as one uniform term and folds each tile's constant offset into its LDS instructions.
   auto set_at = [&](int slot) __attribute__((always_inline)) {
@@ -392,19 +393,11 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     asm volatile("" : "+s"(off));
     return smem + Cfg::OFF_WO + off;
   };
-  auto flags_raw = [&](int b, int4& a, int4& c) __attribute__((always_inline)) {
-    const int4* f = reinterpret_cast<const int4*>(sFlag + (b % 3) * Cfg::NE);
-    a = f[0];
-    c = f[1];
+  auto flags_raw = [&](int b) __attribute__((always_inline)) {
+    return *reinterpret_cast<const u32x2*>(sFlag + (b % 3) * Cfg::NE);
   };
-  auto any_flag = [](int4 a, int4 c) __attribute__((always_inline)) {
-    return ((a.x | a.y | a.z | a.w) | (c.x | c.y | c.z | c.w)) != 0;
-  };
-  auto slow_of = [&](int b) __attribute__((always_inline)) {
-    int4 a, c;
-    flags_raw(b, a, c);
-    return any_flag(a, c);
-  };
+  auto any_flag = [](u32x2 f) __attribute__((always_inline)) { return (f.x | f.y) != 0u; };
+  auto slow_of = [&](int b) __attribute__((always_inline)) { return any_flag(flags_raw(b)); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -515,10 +508,11 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
 
     // e1 handles block b, whose buffers sit in slot sl = b % 3 (slp = (b - 1) % 3), for the
     // wave's half HALF (= half, as a constant: each half has its own code)
-    auto e1 = [&](auto precise_tag, auto half_tag, int b, int sl, int slp, const Raw& cur,
+    auto e1 = [&](auto precise_tag, auto half_tag, auto tail_tag, int b, int sl, int slp, const Raw& cur,
                   Raw& nxt) __attribute__((always_inline)) {
       constexpr bool PRECISE = decltype(precise_tag)::value;
       constexpr int HALF = decltype(half_tag)::value;
+      constexpr bool TAIL = decltype(tail_tag)::value;   // the block may hold identity tokens
       const int tn = b * C;
       const int nval = min(C, T - tn);
       char* sb = set_at(sl);
@@ -527,6 +521,12 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       bf16_t* sKR = reinterpret_cast<bf16_t*>(sb + Cfg::SET_KR);
       float* sG0 = reinterpret_cast<float*>(sb + Cfg::SET_G0);
       float* sD0 = reinterpret_cast<float*>(sb + Cfg::SET_D0);
+      (void)nxt;                               // (loaded by the step: see estep)
+      // D0 of the previous block, for its F (first half only; written a step ago).  Read
+      // first and used before this step's first LDS write, so that the wait for it is for
+      // it alone.
+      float2 dprev = float2{0.0f, 0.0f};
+      if constexpr (HALF == 0) dprev = *reinterpret_cast<const float2*>(set_at(slp) + Cfg::SET_D0 + dpoff);
       Pair<bf16_t> rk[4], rq[4], rz[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -535,15 +535,10 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         if constexpr (SG) rz[t] = Pair<bf16_t>::dup((bf16_t)cur.z[t]);
         else rz[t].u = cur.z[t];
       }
-      (void)nxt;                               // (loaded by the step: see estep)
-      // D0 of the previous block, for its F (first half only; written a step ago).  Read
-      // first and used before this step's first LDS write, so that the wait for it is for
-      // it alone.
-      float2 dprev = float2{0.0f, 0.0f};
-      if constexpr (HALF == 0) dprev = *reinterpret_cast<const float2*>(set_at(slp) + Cfg::SET_D0 + dpoff);
       // Tokens at or past nval (a partial last block, or rows 16..31 when C = 16) are
-      // identity tokens: their k and q read as 0, and z = -inf makes their gate 0.
-      if (nval < 16 * HALF + 16) {
+      // identity tokens: their k and q read as 0, and z = -inf makes their gate 0.  (Blocks
+      // known to be full skip the test: its merge would cost register copies on every step.)
+      if (TAIL && nval < 16 * HALF + 16) {
         const int lim = nval - (16 * HALF + tq);
 #pragma unroll
         for (int t = 0; t < 4; ++t) rz[t].u = t < lim ? rz[t].u : 0xFF80FF80u;
@@ -581,7 +576,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         fp = float2{dprev.x * g0.x, dprev.y * g0.y};
       }
       const unsigned long long bal = __ballot(kact && fminf(sumx, sumy) < -thresh);
-      if (lane == 0) sFlag[sl * Cfg::NE + wave] = bal != 0ull;
+      if (lane == 0) sFlag[sl * Cfg::NE + wave] = bal != 0ull ? 1 : 0;
       const int c = 2 * pair;
       if (HALF == 0 && kact && g == 0) {
         *reinterpret_cast<float2*>(sG0 + c) = g0;
@@ -624,10 +619,11 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     // The same for a PSPLIT wave: one channel (2 pair + par) of the lane's pair, so one
     // gate, one scan and two exponentials per token; the bf16 results of tokens t and
     // t + 2 are packed into one register and stored as two 16-bit halves.
-    auto e1p = [&](auto precise_tag, auto half_tag, int b, int sl, int slp, const Raw& cur)
+    auto e1p = [&](auto precise_tag, auto half_tag, auto tail_tag, int b, int sl, int slp, const Raw& cur)
                    __attribute__((always_inline)) {
       constexpr bool PRECISE = decltype(precise_tag)::value;
       constexpr int HALF = decltype(half_tag)::value;
+      constexpr bool TAIL = decltype(tail_tag)::value;
       const int tn = b * C;
       const int nval = min(C, T - tn);
       char* sb = set_at(sl);
@@ -647,7 +643,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       for (int t = 0; t < 4; ++t) zv[t] = own(cur.z[t]);
       float dprev = 0.0f;
       if constexpr (HALF == 0) dprev = *reinterpret_cast<const float*>(set_at(slp) + Cfg::SET_D0 + dpoff);
-      if (nval < 16 * HALF + 16) {             // identity tokens: gate 0
+      if (TAIL && nval < 16 * HALF + 16) {     // identity tokens: gate 0
         const int lim = nval - (16 * HALF + tq);
 #pragma unroll
         for (int t = 0; t < 4; ++t) zv[t] = t < lim ? zv[t] : -INFINITY;
@@ -669,7 +665,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         fp = dprev * g0;
       }
       const unsigned long long bal = __ballot(kact && sumx < -thresh);
-      if (lane == 0) sFlag[sl * Cfg::NE + wave] = bal != 0ull;
+      if (lane == 0) sFlag[sl * Cfg::NE + wave] = bal != 0ull ? 1 : 0;
       const int c = 2 * pair + par;
       if (HALF == 0 && kact && g == 0) {
         sG0[c] = g0;
@@ -715,7 +711,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     Raw ra, rb, rc;
     load_qkz(0, ra);                           // (blocks past the end read zeros)
     load_qkz(1, rb);
-    auto estep = [&](int s, int sl, int slp, const Raw& cur, Raw& nxt) __attribute__((always_inline)) {
+    auto estep = [&](auto tail_tag, int s, int sl, int slp, Raw& cur, Raw& nxt) __attribute__((always_inline)) {
+      using TT = decltype(tail_tag);
       const int b = s + 2;
       // The loads of the block after next, issued by every step alike (the index is clamped;
       // blocks past the end read zeros), so that the compiler sees the same load count on
@@ -727,34 +724,44 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         using H1 = std::integral_constant<int, 1>;
         if constexpr (PSPLIT) {
           if (precise) {
-            if (half) e1p(std::true_type{}, H1{}, b, sl, slp, cur);
-            else e1p(std::true_type{}, H0{}, b, sl, slp, cur);
+            if (half) e1p(std::true_type{}, H1{}, TT{}, b, sl, slp, cur);
+            else e1p(std::true_type{}, H0{}, TT{}, b, sl, slp, cur);
           } else {
-            if (half) e1p(std::false_type{}, H1{}, b, sl, slp, cur);
-            else e1p(std::false_type{}, H0{}, b, sl, slp, cur);
+            if (half) e1p(std::false_type{}, H1{}, TT{}, b, sl, slp, cur);
+            else e1p(std::false_type{}, H0{}, TT{}, b, sl, slp, cur);
           }
         } else if (precise) {
-          if (half) e1(std::true_type{}, H1{}, b, sl, slp, cur, nxt);
-          else e1(std::true_type{}, H0{}, b, sl, slp, cur, nxt);
+          if (half) e1(std::true_type{}, H1{}, TT{}, b, sl, slp, cur, nxt);
+          else e1(std::true_type{}, H0{}, TT{}, b, sl, slp, cur, nxt);
         } else {
-          if (half) e1(std::false_type{}, H1{}, b, sl, slp, cur, nxt);
-          else e1(std::false_type{}, H0{}, b, sl, slp, cur, nxt);
+          if (half) e1(std::false_type{}, H1{}, TT{}, b, sl, slp, cur, nxt);
+          else e1(std::false_type{}, H0{}, TT{}, b, sl, slp, cur, nxt);
         }
       }
       lds_barrier();
     };
     // three steps per iteration, so that register sets and LDS slots are fixed per position:
-    // step s handles block s + 2 (set and slot (s + 2) % 3) and loads block s + 4.  The loop
-    // runs whole iterations only (no conditional step inside it), the last one or two steps
-    // follow it: nck + 2 steps in all, as for the other stages.
+    // step s handles block s + 2 (set and slot (s + 2) % 3) and loads block s + 4.  The loops
+    // run whole iterations only (no conditional step inside them), the last one or two steps
+    // follow them: nck + 2 steps in all, as for the other stages.  The first loop covers the
+    // iterations whose three blocks hold 32 real tokens each (none when C = 16, where the
+    // second half of every block is identity tokens).
+    const std::true_type tail{};
+    const std::false_type full{};
+    const int nfull = C == 32 ? T / C : 0;
     int s = -2;
-    for (; s + 2 < nck; s += 3) {
-      estep(s, 0, 2, ra, rc);
-      estep(s + 1, 1, 0, rb, ra);
-      estep(s + 2, 2, 1, rc, rb);
+    for (; s + 4 < nfull; s += 3) {
+      estep(full, s, 0, 2, ra, rc);
+      estep(full, s + 1, 1, 0, rb, ra);
+      estep(full, s + 2, 2, 1, rc, rb);
     }
-    if (s < nck) estep(s, 0, 2, ra, rc);
-    if (s + 1 < nck) estep(s + 1, 1, 0, rb, ra);
+    for (; s + 2 < nck; s += 3) {
+      estep(tail, s, 0, 2, ra, rc);
+      estep(tail, s + 1, 1, 0, rb, ra);
+      estep(tail, s + 2, 2, 1, rc, rb);
+    }
+    if (s < nck) estep(tail, s, 0, 2, ra, rc);
+    if (s + 1 < nck) estep(tail, s + 1, 1, 0, rb, ra);
   } else if (wave >= Cfg::NE + Cfg::NV) {
     // ================================================================ W waves
     __builtin_amdgcn_s_setprio(2);             // issue ahead of the E waves (see the V waves)
@@ -1106,9 +1113,9 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       if (paired && vw == 0 && s >= 2) norm_prefetch(s - 2);
     };
 
-    // nf0, nf1: the raw slow flags of block b+1, loaded at the top of the step and only
-    // examined after phase C, so that their read never stalls the start of a step
-    auto vside = [&](auto fast_tag, int b, int4 nf0, int4 nf1) __attribute__((always_inline)) {
+    // nf: the raw slow flags of block b+1, loaded at the top of the step and only examined
+    // after phase C, so that their read never stalls the start of a step
+    auto vside = [&](auto fast_tag, int b, u32x2 nf) __attribute__((always_inline)) {
       constexpr bool FAST = decltype(fast_tag)::value;   // the factorised MFMA path, else token by token
       // Lane indices through an empty asm: the per-lane offsets derived from them are
       // recomputed each block instead of occupying registers across the whole walk.
@@ -1201,7 +1208,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
         // (D) S' = diag(F) (S~ + KR^T U), F = D0 G0' (next block scaled) or D0; KR^T
         // comes from the [token][channel] KR tile through transposing reads
         sched_fence();
-        const bool next_fast = b + 1 < nck && !any_flag(nf0, nf1);
+        const bool next_fast = b + 1 < nck && !any_flag(nf);
         const float* sF = reinterpret_cast<const float*>(sb + (next_fast ? Cfg::SET_F : Cfg::SET_D0));
         constexpr int DH = NMT > 4 ? 2 : 1;    // in halves of four row tiles when K = 128
 #pragma unroll
@@ -1263,7 +1270,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) sacc[mt] = *reinterpret_cast<const floatx4*>(stl + mt * 256);
         wait_vm();                             // the token path's loads
-        if (b + 1 < nck && !any_flag(nf0, nf1)) {
+        if (b + 1 < nck && !any_flag(nf)) {
           const float* sG0n = reinterpret_cast<const float*>(set_base(b + 1) + Cfg::SET_G0);
 #pragma unroll
           for (int mt = 0; mt < NMT; ++mt) sacc[mt] *= *reinterpret_cast<const floatx4*>(sG0n + 16 * mt + 4 * lg);
@@ -1285,23 +1292,21 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     bool slow = nck > 0 && slow_of(0);
     while (s < nck) {
       while (s < nck && !slow) {
-        int4 f0, f1;                           // flags of block s+1 (stale, and unused, past the end)
-        flags_raw(s + 1, f0, f1);
+        const u32x2 f = flags_raw(s + 1);      // flags of block s+1 (stale, and unused, past the end)
         if constexpr (NORM) norm_step(s);
-        if (vact) vside(std::true_type{}, s, f0, f1);
+        if (vact) vside(std::true_type{}, s, f);
         if constexpr (NORM) norm_end(s);
         lds_barrier();
-        slow = s + 1 < nck && any_flag(f0, f1);
+        slow = s + 1 < nck && any_flag(f);
         ++s;
       }
       if (s < nck) {
-        int4 f0, f1;
-        flags_raw(s + 1, f0, f1);
+        const u32x2 f = flags_raw(s + 1);
         if constexpr (NORM) norm_step(s);
-        if (vact) vside(std::false_type{}, s, f0, f1);
+        if (vact) vside(std::false_type{}, s, f);
         if constexpr (NORM) norm_end(s);
         lds_barrier();
-        slow = s + 1 < nck && any_flag(f0, f1);
+        slow = s + 1 < nck && any_flag(f);
         ++s;
       }
     }

@@ -89,8 +89,8 @@ struct PcCfg {
   static constexpr int LD_A = CD + 4;                 // [token][token] fp32
   static constexpr int SZ_TK = CD * LD_TK * 2;
   static constexpr int SZ_TT = CD * LD_CT * 2;
-  // E outputs of one block (triple-buffered): KE, QE, KR, G0, D0, and F = D0 * G0 of the
-  // next block (written with the next block).  A block that takes the token path
+  // E outputs of one block (triple-buffered): KE, QE, KR, G0, D0, beta, and F = D0 * G0 of
+  // the next block (written with the next block).  A block that takes the token path
   // parks the state of the V waves in its set meanwhile, so a set holds at least that.
   static constexpr int SET_KE = 0;
   static constexpr int SET_QE = SET_KE + SZ_TK;
@@ -98,11 +98,11 @@ struct PcCfg {
   static constexpr int SET_G0 = SET_KR + SZ_TK;
   static constexpr int SET_D0 = SET_G0 + KD * 4;
   static constexpr int SET_F = SET_D0 + KD * 4;
-  static constexpr int SET_END = SET_F + KD * 4;
+  static constexpr int SET_BETA = SET_F + KD * 4;
   static constexpr int PARK_BYTES = NV * NMT * 256 * 4;
-  static constexpr int SET_BYTES = round_up(SET_END > PARK_BYTES ? SET_END : PARK_BYTES, 16);
-  // W outputs of one block (double-buffered): P, T diag(beta) (T_00 and T_11 with their
-  // columns scaled by beta, zero elsewhere), -A_10 (columns 0..15, zero in 16..31)
+  static constexpr int SET_BYTES = round_up(SET_BETA + CD * 4 > PARK_BYTES ? SET_BETA + CD * 4 : PARK_BYTES, 16);
+  // W outputs of one block (double-buffered): P, T (T_00 and T_11, zero elsewhere),
+  // -A_10 (columns 0..15, zero in 16..31)
   static constexpr int WO_P = 0;
   static constexpr int WO_T = WO_P + SZ_TT;
   static constexpr int WO_A10 = WO_T + SZ_TT;
@@ -768,17 +768,17 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     const int ww = wave - (Cfg::NE + Cfg::NV);
     // The W waves also stage the next blocks' inputs that are not per channel pair: the v
     // tile (waves 0 .. NNT-1 of the stage, 16 columns each, slot 2*row + half) and beta.
-    // beta enters through the two inverse waves only (wave I: tokens 16*I + l16), which scale
-    // the rows of A_II by it and fold it into the columns of T, so V never reads it.  Both
-    // loads are issued after the wave's last LDS read of a step and waited for at the start
-    // of the next one, so their latency hides behind the barrier (an LDS DMA in flight would
-    // make every LDS read wait for it).  Tokens past the head's range read as 0.
+    // Each W wave loads beta of the rows its tiles scale (tokens 16*I + l16); the last one
+    // loads all of the block's tokens and writes them to LDS for the V waves.  Both are
+    // issued after the wave's last LDS read of a step and waited for at the start of the
+    // next one, so their latency hides behind the barrier (an LDS DMA in flight would make
+    // every LDS read wait for it).  Tokens past the head's range read as 0.
     const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(v + tb * V, (unsigned)(T * V * 2));
     const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(beta + tb, (unsigned)(T * 2));
-    const int btok = 16 * ww + l16;
+    const int btok = ww == Cfg::NW - 1 ? lane : (ww == 0 ? 0 : 16) + l16;
     auto load_beta = [&](int b) __attribute__((always_inline)) {
       const unsigned off = btok < C ? (unsigned)((b * C + btok) * 2) : kOOB;
-      return ww < NB ? __builtin_amdgcn_raw_buffer_load_b16(rs_b, off, 0, 0) : (unsigned short)0;
+      return __builtin_amdgcn_raw_buffer_load_b16(rs_b, off, 0, 0);
     };
     auto dma_v = [&](int b) __attribute__((always_inline)) {
       if (ww < NNT) {
@@ -822,8 +822,9 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
           const float bi = -rbeta;             // beta of row i (the tile is -A: KE is stored negated)
           *reinterpret_cast<floatx4*>(sA + i * LD_A + j0) =
               floatx4{bi * vals[0], bi * vals[1], bi * vals[2], bi * vals[3]};
-        } else if (isA) {                      // A_10: bf16, negated (the tile is -A_10), for V
-          store4_bf16(sA10 + l16 * LD_CT + perm32(j0), vals[0], vals[1], vals[2], vals[3]);
+        } else if (isA) {                      // A_10: bf16, negated, for V
+          const float nb = rbeta;              // (the tile is -A_10)
+          store4_bf16(sA10 + l16 * LD_CT + perm32(j0), nb * vals[0], nb * vals[1], nb * vals[2], nb * vals[3]);
         } else {
           store4_bf16(sP + i * LD_CT + perm32(j0), vals[0], vals[1], vals[2], vals[3]);
         }
@@ -894,7 +895,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             wsD[(8 * h + i) * WL + lane] = t[i];
-            sT[(16 * I + 8 * h + i) * LD_CT + perm32(16 * I + lane)] = f2bf(t[i] * rbeta);
+            sT[(16 * I + 8 * h + i) * LD_CT + perm32(16 * I + lane)] = f2bf(t[i]);
           }
         }
         const int ki = lane >> 3, j = lane & 7;
@@ -922,10 +923,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
             u0 = fmaf(b0[k4], c0[k4], u0);
             u1 = fmaf(b1[k4], c1[k4], u1);
           }
-          // beta of column j: this lane's own (lane & 15 = j) or that of the lane 8 below it
-          const float bj = __int_as_float(
-              __builtin_amdgcn_update_dpp(__float_as_int(rbeta), __float_as_int(rbeta), 0x118, 0xf, 0xf, false));
-          sT[(16 * I + 8 + ki) * LD_CT + perm32(16 * I + j)] = f2bf(-(u0 + u1) * bj);
+          sT[(16 * I + 8 + ki) * LD_CT + perm32(16 * I + j)] = f2bf(-(u0 + u1));
         }
       }
     };
@@ -936,6 +934,8 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       wait_vm();                               // beta of block b, v of block b+1
       if (b >= 0 && b < nck) {
         if (!slow_of(b)) wstage(b, bf2f(wbeta));
+        if (ww == Cfg::NW - 1 && lane < CD)
+          reinterpret_cast<float*>(set_base(b) + Cfg::SET_BETA)[lane] = bf2f(wbeta);
       }
       if (b + 1 < nck) wbeta = load_beta(b + 1);
       if (s + 2 < nck) dma_v(s + 2);
@@ -1128,6 +1128,7 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
       const bf16_t* sKE = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KE);
       const bf16_t* sQE = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_QE);
       const bf16_t* sKR = reinterpret_cast<const bf16_t*>(sb + Cfg::SET_KR);
+      const float* sBeta = reinterpret_cast<const float*>(sb + Cfg::SET_BETA);
       char* wb = wo_base(b);
       const bf16_t* sP = reinterpret_cast<const bf16_t*>(wb + Cfg::WO_P);
       const bf16_t* sT = reinterpret_cast<const bf16_t*>(wb + Cfg::WO_T);
@@ -1178,22 +1179,23 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
               oT[I] = mfma_bf16(sp[j], fq[I][j], oT[I]);
             }
         }
-        // (C) U_0 = T_00 Y_0, U_1 = T_11 (Y_1 - A_10 U_0): the W stage folds diag(beta) into the
-        // columns of T (T_II diag(beta_I)), and fa10 holds -A_10
+        // (C) U_0 = T_00 Z_0, U_1 = T_11 (Z_1 - A_10 U_0), Z = diag(beta) Y (fa10 holds -beta A_10)
         short8 ub;
         {
           short8 ft[NB], fp[NB], fa10;
+          floatx4 bt[NB];
 #pragma unroll
           for (int I = 0; I < NB; ++I) {
             ft[I] = lds_frag(sT, LD_CT, 16 * I, 0, ln);
             fp[I] = lds_frag(sP, LD_CT, 16 * I, 0, ln);
+            bt[I] = *reinterpret_cast<const floatx4*>(sBeta + 16 * I + 4 * lg);
           }
           if (NB == 2) fa10 = lds_frag(sA10, LD_CT, 0, 0, ln);
           sched_fence();
           floatx4 U[2];
-          U[0] = mfma_bf16(ft[0], acc_perm(Y[0], zero4()), zero4());
+          U[0] = mfma_bf16(ft[0], acc_perm(Y[0] * bt[0], zero4()), zero4());
           if (NB == 2) {
-            const floatx4 Z1 = mfma_bf16(fa10, acc_perm(U[0], zero4()), Y[1]);
+            const floatx4 Z1 = mfma_bf16(fa10, acc_perm(U[0], zero4()), Y[1] * bt[NB - 1]);
             U[1] = mfma_bf16(ft[NB - 1], acc_perm(zero4(), Z1), zero4());
           } else {
             U[1] = zero4();

@@ -1117,9 +1117,13 @@ chunk_fwd_pc_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, 
     // after phase C, so that their read never stalls the start of a step
     auto vside = [&](auto fast_tag, int b, u32x2 nf) __attribute__((always_inline)) {
       constexpr bool FAST = decltype(fast_tag)::value;   // the factorised MFMA path, else token by token
-      // The per-lane parts of the LDS and store offsets stay in registers across the walk
-      // (about 25 fewer address instructions per step than recomputing them each block).
+      // KD = 128: the per-lane parts of the LDS and store offsets stay in registers across
+      // the walk (about 25 fewer address instructions per step than recomputing them each
+      // block; that workload is bound by the socket's power, so fewer instructions win).
+      // Smaller KD: the lane index passes through an empty asm, which makes the offsets be
+      // recomputed each block (measured faster there, where the step's latency bounds).
       int ln = lane;
+      if constexpr (KD < 128) asm volatile("" : "+v"(ln));
       ln &= 63;                                // a known range lets LDS offsets fold into the loads
       const int lg = ln >> 4, ll = ln & 15;
       const int t0c = b * C;

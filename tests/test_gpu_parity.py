@@ -185,6 +185,10 @@ CASES = [  # (dtype, K, V, chunk, T)
     ("f32", 64, 16, 32, 77), ("f32", 128, 128, 64, 100), ("f32", 128, 32, 16, 40), ("f32", 64, 128, 64, 129),
     ("bf16", 32, 32, 32, 97), ("bf16", 64, 64, 64, 200), ("bf16", 128, 128, 64, 150), ("bf16", 128, 64, 32, 65),
     ("bf16", 16, 8, 16, 33), ("bf16", 8, 128, 64, 64), ("bf16", 64, 128, 16, 50),
+    # the gate/decay stage runs whole blocks through a loop without the identity-token test and the
+    # rest (a ragged last block, the steps past the end) through the general one: 7 whole blocks and
+    # a ragged eighth, and 9 whole blocks (three iterations of the first loop, then the final steps)
+    ("bf16", 128, 128, 64, 229), ("bf16", 64, 64, 32, 288),
 ]
 
 

@@ -50,6 +50,71 @@ __global__ void __launch_bounds__(256) gate_kernel(const Tin* __restrict__ z, co
   }
 }
 
+// The same gate for K % 8 == 0 and 16-byte aligned buffers: thread tid covers eight
+// consecutive channels 8 * (cb + tid % KC) .. +7 of every (256 / KC)-th token row, so each
+// row access is one 16-byte load of z (two for fp32) and four 16-byte stores of g and alpha.
+template <typename Tin>
+__global__ void __launch_bounds__(256) gate_kernel8(const Tin* __restrict__ z, const float* __restrict__ A_log,
+                                                    const float* __restrict__ dt_bias, float* __restrict__ g_out,
+                                                    float* __restrict__ alpha_out, int H, int T, int K, int ntile) {
+  const int wg = blockIdx.x;
+  const int bh = wg / ntile, tile = wg - bh * ntile;
+  const int h = bh % H;
+  const int t0 = tile * kGateTile, t1 = min(T, t0 + kGateTile);
+  const float mult = gate_multiplier(A_log[h]);
+  const int tid = threadIdx.x;
+  const int K8 = K / 8;
+  for (int cb = 0; cb < K8; cb += 256) {
+    const int KC = min(K8 - cb, 256);          // channel groups of this pass
+    const int rpp = 256 / KC;                  // token rows per pass
+    const int r = tid / KC, c = 8 * (cb + tid % KC);
+    if (r >= rpp) continue;
+    float db[8];
+#pragma unroll
+    for (int j = 0; j < 8; j += 4) {
+      const float4 d4 = dt_bias ? *reinterpret_cast<const float4*>(dt_bias + h * K + c + j) : float4{0, 0, 0, 0};
+      db[j] = d4.x;
+      db[j + 1] = d4.y;
+      db[j + 2] = d4.z;
+      db[j + 3] = d4.w;
+    }
+    for (int t = t0 + r; t < t1; t += rpp) {
+      const size_t idx = ((size_t)bh * T + t) * K + c;
+      float x[8];
+      if constexpr (sizeof(Tin) == 2) {
+        const uint4 w = *reinterpret_cast<const uint4*>(z + idx);
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[2 * j] = __uint_as_float(u[j] << 16);
+          x[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; j += 4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(z) + idx + j);
+          x[j] = v4.x;
+          x[j + 1] = v4.y;
+          x[j + 2] = v4.z;
+          x[j + 3] = v4.w;
+        }
+      }
+      float gv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) gv[j] = -mult * softplus_f(x[j] + db[j], true);
+      *reinterpret_cast<float4*>(g_out + idx) = float4{gv[0], gv[1], gv[2], gv[3]};
+      *reinterpret_cast<float4*>(g_out + idx + 4) = float4{gv[4], gv[5], gv[6], gv[7]};
+      if (alpha_out) {
+        float av[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) av[j] = fast_exp2(gv[j] * kLog2e);
+        *reinterpret_cast<float4*>(alpha_out + idx) = float4{av[0], av[1], av[2], av[3]};
+        *reinterpret_cast<float4*>(alpha_out + idx + 4) = float4{av[4], av[5], av[6], av[7]};
+      }
+    }
+  }
+}
+
 // Reverse of the gate for a cotangent dg on g.  With x = z + dt_bias and
 // m = exp(clamp(A_log)):  dz = -m sigmoid(x) dg  (the slope of softplus is the sigmoid);
 // d dt_bias[h][c] = dz summed over batch and time; dA_log[h] = dg g summed over batch,
@@ -210,8 +275,13 @@ hipError_t launch_gate(const void* z, const float* A_log, const float* dt_bias, 
   const long long blocks = (long long)B * H * ntile;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gate_kernel<Tin>, dim3((unsigned)blocks), dim3(256), 0, s, (const Tin*)z, A_log, dt_bias, g,
-                     alpha, H, T, K, ntile);
+  const uintptr_t al = (uintptr_t)z | (uintptr_t)g | (uintptr_t)alpha | (uintptr_t)dt_bias;
+  if (K % 8 == 0 && (al & 15) == 0)
+    hipLaunchKernelGGL(gate_kernel8<Tin>, dim3((unsigned)blocks), dim3(256), 0, s, (const Tin*)z, A_log, dt_bias, g,
+                       alpha, H, T, K, ntile);
+  else
+    hipLaunchKernelGGL(gate_kernel<Tin>, dim3((unsigned)blocks), dim3(256), 0, s, (const Tin*)z, A_log, dt_bias, g,
+                       alpha, H, T, K, ntile);
   return hipGetLastError();
 }
 

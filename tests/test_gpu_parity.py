@@ -27,18 +27,26 @@ _check = check
 
 
 # ----------------------------------------------------------------------------- gate
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_gate(dtype):
+# K % 8 == 0 with 16-byte aligned buffers takes the eight-channel kernel (K = 2056: two
+# channel passes); K = 12 and a z that starts 8 bytes off a 16-byte boundary take the
+# one-channel kernel
+@pytest.mark.parametrize("dtype,K,off", [("f32", 64, 0), ("bf16", 64, 0), ("f32", 12, 0), ("bf16", 2056, 0),
+                                         ("f32", 64, 2)])
+def test_gate(dtype, K, off):
     rng = np.random.default_rng(11)
-    B, H, T, K = 2, 3, 37, 64
+    B, H, T = 2, 3, 37
     z = rng.standard_normal((B, H, T, K)).astype(np.float32) * 4
     z[0, 0, 0, :8] = [-50, -20, -5, 0, 5, 20, 50, 1]
     if dtype == "bf16":
         z = ks.round_bf16(z)
     A_log = np.array([-3.0, 0.0, 25.0], dtype=np.float32)
     dt = (0.5 * rng.standard_normal((H, K))).astype(np.float32)
-    g, a = kda.gate(to_dev(z, torch.bfloat16 if dtype == "bf16" else torch.float32),
-                    to_dev(A_log, torch.float32), to_dev(dt, torch.float32))
+    zt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    zd = to_dev(z, zt)
+    if off:
+        buf = torch.empty(zd.numel() + off, dtype=zt, device=zd.device)
+        zd = buf[off:].view(zd.shape).copy_(zd)
+    g, a = kda.gate(zd, to_dev(A_log, torch.float32), to_dev(dt, torch.float32))
     gr, ar = R.gate(z, A_log, dt)
     _check("g", host(g), gr, 2e-6)
     _check("alpha", host(a), ar, 2e-6)

@@ -237,8 +237,26 @@ def gate_bench(steps, warmup):
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / steps
     nbytes = B * H * T * K * (2 + 4 + 4)
-    print(json.dumps({"metric": "gate bandwidth (kda_gate, g and alpha)", "value": round(nbytes / us / 1e3, 1),
-                      "unit": "GB/s", "frac_of_8TBps": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+    del z
+    # Ceilings measured in the same run: a plain device copy (read + write) and a write-only
+    # fill of the size of the gate's two outputs (four fifths of the gate's bytes are writes).
+    copy_gbs = copy_bandwidth_gbs(torch)
+    fill = torch.empty(2 * B * H * T * K, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        fill.fill_(1.0)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        fill.fill_(1.0)
+    b.record()
+    torch.cuda.synchronize()
+    fill_gbs = fill.numel() * 4 / (a.elapsed_time(b) * 1e-3 / steps) / 1e9
+    del fill
+    gbs = nbytes / us / 1e3
+    print(json.dumps({"metric": "gate bandwidth (kda_gate, g and alpha)", "value": round(gbs, 1),
+                      "unit": "GB/s", "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4),
+                      "copy_GBps": round(copy_gbs, 1), "frac_of_copy": round(gbs / copy_gbs, 4),
+                      "write_fill_GBps": round(fill_gbs, 1), "frac_of_write_fill": round(gbs / fill_gbs, 4),
                       "us_per_call": round(us, 2), "bytes_per_call": nbytes, "steps": steps,
                       "config": {"B": B, "H": H, "T": T, "K": K, "z": "bf16", "outputs": "f32 g, alpha"},
                       "note": "HIP events around the calls (each allocates its two outputs through torch's "

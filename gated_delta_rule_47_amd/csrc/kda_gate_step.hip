@@ -21,7 +21,8 @@
 
 namespace kda {
 
-constexpr int kGateTile = 64;
+constexpr int kGateTile = 32;
+constexpr int kGate4Threads = 512;            // workgroup size of gate_kernel4
 
 // Thread tid covers channel cb + tid % KC of every (256 / KC)-th token row of the tile,
 // for each pass cb of up to 256 channels.
@@ -50,11 +51,53 @@ __global__ void __launch_bounds__(256) gate_kernel(const Tin* __restrict__ z, co
   }
 }
 
-// The same gate for K % 8 == 0 and 16-byte aligned buffers: thread tid covers eight
-// consecutive channels 8 * (cb + tid % KC) .. +7 of every (256 / KC)-th token row, so each
-// row access is one 16-byte load of z (two for fp32) and four 16-byte stores of g and alpha.
+// The same gate for K % 4 == 0 and aligned buffers (g, alpha, dt_bias 16 bytes, z four
+// elements).  A tile's rows t0 .. t1-1 are one contiguous range of (t1 - t0) * K elements
+// in z, g and alpha; thread tid takes the four-element groups tid, tid + kGate4Threads, ... of that
+// range, so the 64 lanes of a wave read and write one gap-free span per instruction (16
+// bytes per lane of g and of alpha, 8 or 16 of z).  The group's channel advances by
+// kGate4Threads mod (K / 4) groups per pass, without a division.
+template <typename Tin, bool FIXED>
+__device__ __forceinline__ void gate_range4(const Tin* __restrict__ z, const float* __restrict__ db_h,
+                                            float* __restrict__ g_out, float* __restrict__ alpha_out, size_t base,
+                                            int ngroups, int K4, float mult) {
+  const int step = FIXED ? 0 : kGate4Threads % K4;
+  int cg = threadIdx.x % K4;
+  float4 d4 = db_h ? *reinterpret_cast<const float4*>(db_h + 4 * cg) : float4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 2
+  for (int e = threadIdx.x; e < ngroups; e += kGate4Threads) {
+    const size_t idx = base + 4 * (size_t)e;
+    float x[4];
+    if constexpr (sizeof(Tin) == 2) {
+      const uint2 w = *reinterpret_cast<const uint2*>(z + idx);
+      x[0] = __uint_as_float(w.x << 16);
+      x[1] = __uint_as_float(w.x & 0xffff0000u);
+      x[2] = __uint_as_float(w.y << 16);
+      x[3] = __uint_as_float(w.y & 0xffff0000u);
+    } else {
+      const float4 v4 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(z) + idx);
+      x[0] = v4.x;
+      x[1] = v4.y;
+      x[2] = v4.z;
+      x[3] = v4.w;
+    }
+    if (!FIXED && db_h) d4 = *reinterpret_cast<const float4*>(db_h + 4 * cg);
+    const float gv[4] = {-mult * softplus_f(x[0] + d4.x, true), -mult * softplus_f(x[1] + d4.y, true),
+                         -mult * softplus_f(x[2] + d4.z, true), -mult * softplus_f(x[3] + d4.w, true)};
+    *reinterpret_cast<float4*>(g_out + idx) = float4{gv[0], gv[1], gv[2], gv[3]};
+    if (alpha_out)
+      *reinterpret_cast<float4*>(alpha_out + idx) =
+          float4{fast_exp2(gv[0] * kLog2e), fast_exp2(gv[1] * kLog2e), fast_exp2(gv[2] * kLog2e),
+                 fast_exp2(gv[3] * kLog2e)};
+    if (!FIXED) {
+      cg += step;
+      if (cg >= K4) cg -= K4;
+    }
+  }
+}
+
 template <typename Tin>
-__global__ void __launch_bounds__(256) gate_kernel8(const Tin* __restrict__ z, const float* __restrict__ A_log,
+__global__ void __launch_bounds__(kGate4Threads) gate_kernel4(const Tin* __restrict__ z, const float* __restrict__ A_log,
                                                     const float* __restrict__ dt_bias, float* __restrict__ g_out,
                                                     float* __restrict__ alpha_out, int H, int T, int K, int ntile) {
   const int wg = blockIdx.x;
@@ -62,57 +105,14 @@ __global__ void __launch_bounds__(256) gate_kernel8(const Tin* __restrict__ z, c
   const int h = bh % H;
   const int t0 = tile * kGateTile, t1 = min(T, t0 + kGateTile);
   const float mult = gate_multiplier(A_log[h]);
-  const int tid = threadIdx.x;
-  const int K8 = K / 8;
-  for (int cb = 0; cb < K8; cb += 256) {
-    const int KC = min(K8 - cb, 256);          // channel groups of this pass
-    const int rpp = 256 / KC;                  // token rows per pass
-    const int r = tid / KC, c = 8 * (cb + tid % KC);
-    if (r >= rpp) continue;
-    float db[8];
-#pragma unroll
-    for (int j = 0; j < 8; j += 4) {
-      const float4 d4 = dt_bias ? *reinterpret_cast<const float4*>(dt_bias + h * K + c + j) : float4{0, 0, 0, 0};
-      db[j] = d4.x;
-      db[j + 1] = d4.y;
-      db[j + 2] = d4.z;
-      db[j + 3] = d4.w;
-    }
-    for (int t = t0 + r; t < t1; t += rpp) {
-      const size_t idx = ((size_t)bh * T + t) * K + c;
-      float x[8];
-      if constexpr (sizeof(Tin) == 2) {
-        const uint4 w = *reinterpret_cast<const uint4*>(z + idx);
-        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          x[2 * j] = __uint_as_float(u[j] << 16);
-          x[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; j += 4) {
-          const float4 v4 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(z) + idx + j);
-          x[j] = v4.x;
-          x[j + 1] = v4.y;
-          x[j + 2] = v4.z;
-          x[j + 3] = v4.w;
-        }
-      }
-      float gv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) gv[j] = -mult * softplus_f(x[j] + db[j], true);
-      *reinterpret_cast<float4*>(g_out + idx) = float4{gv[0], gv[1], gv[2], gv[3]};
-      *reinterpret_cast<float4*>(g_out + idx + 4) = float4{gv[4], gv[5], gv[6], gv[7]};
-      if (alpha_out) {
-        float av[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) av[j] = fast_exp2(gv[j] * kLog2e);
-        *reinterpret_cast<float4*>(alpha_out + idx) = float4{av[0], av[1], av[2], av[3]};
-        *reinterpret_cast<float4*>(alpha_out + idx + 4) = float4{av[4], av[5], av[6], av[7]};
-      }
-    }
-  }
+  const int K4 = K >> 2;
+  const int ngroups = (t1 - t0) * K4;
+  const size_t base = ((size_t)bh * T + t0) * K;
+  const float* db_h = dt_bias ? dt_bias + (size_t)h * K : nullptr;
+  if (kGate4Threads % K4 == 0)                 // each thread keeps one channel group
+    gate_range4<Tin, true>(z, db_h, g_out, alpha_out, base, ngroups, K4, mult);
+  else
+    gate_range4<Tin, false>(z, db_h, g_out, alpha_out, base, ngroups, K4, mult);
 }
 
 // Reverse of the gate for a cotangent dg on g.  With x = z + dt_bias and
@@ -275,9 +275,9 @@ hipError_t launch_gate(const void* z, const float* A_log, const float* dt_bias, 
   const long long blocks = (long long)B * H * ntile;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  const uintptr_t al = (uintptr_t)z | (uintptr_t)g | (uintptr_t)alpha | (uintptr_t)dt_bias;
-  if (K % 8 == 0 && (al & 15) == 0)
-    hipLaunchKernelGGL(gate_kernel8<Tin>, dim3((unsigned)blocks), dim3(256), 0, s, (const Tin*)z, A_log, dt_bias, g,
+  const uintptr_t al = (uintptr_t)g | (uintptr_t)alpha | (uintptr_t)dt_bias;
+  if (K % 4 == 0 && (al & 15) == 0 && ((uintptr_t)z & (4 * sizeof(Tin) - 1)) == 0)
+    hipLaunchKernelGGL(gate_kernel4<Tin>, dim3((unsigned)blocks), dim3(kGate4Threads), 0, s, (const Tin*)z, A_log, dt_bias, g,
                        alpha, H, T, K, ntile);
   else
     hipLaunchKernelGGL(gate_kernel<Tin>, dim3((unsigned)blocks), dim3(256), 0, s, (const Tin*)z, A_log, dt_bias, g,

@@ -27,11 +27,13 @@ _check = check
 
 
 # ----------------------------------------------------------------------------- gate
-# K % 8 == 0 with 16-byte aligned buffers takes the eight-channel kernel (K = 2056: two
-# channel passes); K = 12 and a z that starts 8 bytes off a 16-byte boundary take the
-# one-channel kernel
+# K % 4 == 0 with aligned buffers takes the four-channel kernel: at K = 64 each thread
+# keeps one channel group, at K = 12 and K = 2056 (more groups than threads) the group
+# advances every pass; a bf16 z 8 bytes off a 16-byte boundary still qualifies.  An fp32
+# z 8 bytes off, or a bf16 z 4 bytes off, takes the one-channel kernel.  T = 37 leaves a
+# ragged last tile.
 @pytest.mark.parametrize("dtype,K,off", [("f32", 64, 0), ("bf16", 64, 0), ("f32", 12, 0), ("bf16", 2056, 0),
-                                         ("f32", 64, 2)])
+                                         ("bf16", 64, 4), ("f32", 64, 2), ("bf16", 64, 2)])
 def test_gate(dtype, K, off):
     rng = np.random.default_rng(11)
     B, H, T = 2, 3, 37

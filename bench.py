@@ -263,6 +263,45 @@ def gate_bench(steps, warmup):
                               "caching allocator)"}))
 
 
+def gate_bwd_bench(steps, warmup):
+    """The gate adjoint (kda_gate_bwd: dz, dA_log, d dt_bias) on the long workload's gate
+    shape (4 x 32 heads x 16384 tokens x 128 channels, bf16 z, fp32 dg and dz): 10 bytes
+    per element (z 2, dg 4 read; dz 4 written), plus the small per-tile partial sums."""
+    import torch
+    import gated_delta_rule_47_amd as kda
+    dev = torch.device("cuda:0")
+    B, H, T, K = 4, 32, 16384, 128
+    gen = torch.Generator(device=dev).manual_seed(12)
+    z = torch.randn(B, H, T, K, device=dev, generator=gen).to(torch.bfloat16)
+    dg = torch.randn(B, H, T, K, device=dev, generator=gen)
+    A_log = torch.linspace(-2.0, 1.0, H, device=dev)
+    dt_bias = 0.5 * torch.randn(H, K, device=dev, generator=gen)
+    dz = torch.empty_like(dg)
+    ws = torch.empty(max(kda.gate_bwd_workspace_bytes(B, H, T, K), 1), dtype=torch.uint8, device=dev)
+    call = lambda: kda.gate_bwd(z, A_log, dt_bias, dg, workspace=ws, dz_out=dz)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    nbytes = B * H * T * K * (2 + 4 + 4)
+    del z, dg, dz
+    copy_gbs = copy_bandwidth_gbs(torch)
+    gbs = nbytes / us / 1e3
+    print(json.dumps({"metric": "gate adjoint bandwidth (kda_gate_bwd: dz, dA_log, d dt_bias)", "value": round(gbs, 1),
+                      "unit": "GB/s", "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4),
+                      "copy_GBps": round(copy_gbs, 1), "frac_of_copy": round(gbs / copy_gbs, 4),
+                      "us_per_call": round(us, 2), "bytes_per_call": nbytes, "steps": steps,
+                      "config": {"B": B, "H": H, "T": T, "K": K, "z": "bf16", "dg": "f32", "outputs": "f32 dz"},
+                      "note": "HIP events around the calls (caller workspace and dz; three fifths of the bytes "
+                              "are reads)"}))
+
+
 FP32_PEAK_TFLOPS = 157.3      # MI355X dense fp32 (matrix), published
 
 
@@ -359,6 +398,8 @@ def main():
                          "rows 1 + N(0, 0.1^2), eps 1e-6); a separate metric line")
     ap.add_argument("--gate", action="store_true",
                     help="instead of the benchmark, time the standalone gate (kda_gate) on the long workload's z")
+    ap.add_argument("--gate-bwd", action="store_true",
+                    help="instead of the benchmark, time the gate adjoint (kda_gate_bwd) on the long workload's z")
     ap.add_argument("--adjoint", action="store_true",
                     help="instead of the benchmark, time kda_chunk_bwd on the adjoint workload (fp32)")
     args = ap.parse_args()
@@ -377,6 +418,9 @@ def main():
         return
     if args.gate:
         gate_bench(args.steps, min(args.warmup, 10))
+        return
+    if args.gate_bwd:
+        gate_bwd_bench(args.steps, min(args.warmup, 10))
         return
     if args.adjoint:
         adjoint_bench(args.steps, min(args.warmup, 5))

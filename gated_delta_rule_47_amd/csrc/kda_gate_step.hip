@@ -174,33 +174,128 @@ __global__ void __launch_bounds__(256) gate_bwd_tile_kernel(const Tin* __restric
   }
 }
 
-__global__ void __launch_bounds__(256) gate_bwd_reduce_kernel(const float* __restrict__ part,
-                                                              const float* __restrict__ A_log, float* dA_log,
-                                                              float* d_dt_bias, int B, int H, int K, int ntile) {
-  __shared__ float s_red[256];
+// The same first pass for K % 4 == 0, K / 4 dividing the workgroup size, and aligned
+// buffers (dg, dz, dt_bias and the workspace 16 bytes, z four elements): the tile's rows
+// are one contiguous range, thread tid takes its four-element groups tid, tid + NT, ...
+// (gap-free 16-byte accesses per wave), and since NT is a multiple of K / 4 every group of
+// a thread has the same four channels, whose sums it keeps in registers; the threads of a
+// channel group then add theirs in a fixed order.
+constexpr int kGateBwd4Threads = 1024;
+
+template <typename Tin>
+__global__ void __launch_bounds__(kGateBwd4Threads) gate_bwd_tile_kernel4(
+    const Tin* __restrict__ z, const float* __restrict__ A_log, const float* __restrict__ dt_bias, const float* dg,
+    float* dz, float* __restrict__ part, int H, int T, int K, int ntile) {
+  constexpr int NT = kGateBwd4Threads;
+  __shared__ float4 s_dz[NT], s_gg[NT];
+  const int wg = blockIdx.x;
+  const int bh = wg / ntile, tile = wg % ntile;
+  const int h = bh % H;
+  const int t0 = tile * kGateBwdTile, t1 = min(T, t0 + kGateBwdTile);
+  const float m = gate_multiplier(A_log[h]);
+  const int tid = threadIdx.x;
+  const int K4 = K >> 2;
+  const int cg = tid % K4;
+  const float4 d4 = dt_bias ? *reinterpret_cast<const float4*>(dt_bias + (size_t)h * K + 4 * cg)
+                            : float4{0.0f, 0.0f, 0.0f, 0.0f};
+  const float db[4] = {d4.x, d4.y, d4.z, d4.w};
+  const int ngroups = (t1 - t0) * K4;
+  const size_t base = ((size_t)bh * T + t0) * K;
+  float sdz[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sgg[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int e = tid; e < ngroups; e += NT) {
+    const size_t idx = base + 4 * (size_t)e;
+    float x[4];
+    if constexpr (sizeof(Tin) == 2) {
+      const uint2 w = *reinterpret_cast<const uint2*>(z + idx);
+      x[0] = __uint_as_float(w.x << 16);
+      x[1] = __uint_as_float(w.x & 0xffff0000u);
+      x[2] = __uint_as_float(w.y << 16);
+      x[3] = __uint_as_float(w.y & 0xffff0000u);
+    } else {
+      const float4 v4 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(z) + idx);
+      x[0] = v4.x;
+      x[1] = v4.y;
+      x[2] = v4.z;
+      x[3] = v4.w;
+    }
+    const float4 g4 = *reinterpret_cast<const float4*>(dg + idx);
+    const float dgv[4] = {g4.x, g4.y, g4.z, g4.w};
+    float d[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float xv = x[j] + db[j];
+      const float g = -m * softplus_f(xv, true);
+      const float sig = fast_rcp(1.0f + fast_exp2(-xv * kLog2e));
+      d[j] = -m * sig * dgv[j];
+      sdz[j] += d[j];
+      sgg[j] += dgv[j] * g;
+    }
+    if (dz) *reinterpret_cast<float4*>(dz + idx) = float4{d[0], d[1], d[2], d[3]};   // (dz may be dg: read above)
+  }
+  s_dz[tid] = float4{sdz[0], sdz[1], sdz[2], sdz[3]};
+  s_gg[tid] = float4{sgg[0], sgg[1], sgg[2], sgg[3]};
+  __syncthreads();
+  if (tid < K4) {                              // channel group tid: threads tid, tid + K4, ...
+    float4 a = s_dz[tid], b = s_gg[tid];
+    for (int r = tid + K4; r < NT; r += K4) {
+      const float4 u = s_dz[r], w = s_gg[r];
+      a = float4{a.x + u.x, a.y + u.y, a.z + u.z, a.w + u.w};
+      b = float4{b.x + w.x, b.y + w.y, b.z + w.z, b.w + w.w};
+    }
+    float* pw = part + (size_t)wg * 2 * K;
+    *reinterpret_cast<float4*>(pw + 4 * tid) = a;
+    *reinterpret_cast<float4*>(pw + K + 4 * tid) = b;
+  }
+}
+
+// Pass 2, one workgroup of 1024 threads per head: thread (s, j) adds column j of the tile
+// sums (2K columns: the dz sums, then the dg g sums) over the tiles s, s + 4, ... of each
+// batch, 256 columns at a time; the four slices meet in LDS in a fixed order, and the
+// dg g column totals are added by a fixed tree, so the result does not depend on
+// scheduling.
+constexpr int kGateRedCols = 256, kGateRedSlices = 4;
+
+__global__ void __launch_bounds__(kGateRedCols* kGateRedSlices) gate_bwd_reduce_kernel(
+    const float* __restrict__ part, const float* __restrict__ A_log, float* dA_log, float* d_dt_bias, int B, int H,
+    int K, int ntile) {
+  __shared__ float s_red[kGateRedSlices][kGateRedCols];
   const int h = blockIdx.x;
   const int tid = threadIdx.x;
-  float gg = 0.0f;
-  for (int c = tid; c < K; c += 256) {
-    float sdz = 0.0f, sgg = 0.0f;
-    for (int b = 0; b < B; ++b)
-      for (int tile = 0; tile < ntile; ++tile) {
-        const float* pw = part + ((size_t)(b * H + h) * ntile + tile) * 2 * K;
-        sdz += pw[c];
-        sgg += pw[K + c];
+  const int col = tid % kGateRedCols, sl = tid / kGateRedCols;
+  float gg = 0.0f;                             // slice 0: this column's dg g totals
+  for (int c0 = 0; c0 < 2 * K; c0 += kGateRedCols) {
+    const int j = c0 + col;
+    float acc = 0.0f;
+    if (j < 2 * K) {
+      for (int b = 0; b < B; ++b) {
+        const float* pc = part + (size_t)(b * H + h) * ntile * 2 * K + j;
+#pragma unroll 8
+        for (int tile = sl; tile < ntile; tile += kGateRedSlices) acc += pc[(size_t)tile * 2 * K];
       }
-    if (d_dt_bias) d_dt_bias[h * K + c] = sdz;
-    gg += sgg;
+    }
+    s_red[sl][col] = acc;
+    __syncthreads();
+    if (sl == 0 && j < 2 * K) {
+      float t = s_red[0][col];
+#pragma unroll
+      for (int q = 1; q < kGateRedSlices; ++q) t += s_red[q][col];
+      if (j < K) {
+        if (d_dt_bias) d_dt_bias[h * K + j] = t;
+      } else {
+        gg += t;
+      }
+    }
+    __syncthreads();
   }
-  s_red[tid] = gg;
+  if (sl == 0) s_red[0][col] = gg;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) s_red[tid] += s_red[tid + w];
+  for (int w = kGateRedCols / 2; w > 0; w >>= 1) {
+    if (sl == 0 && col < w) s_red[0][col] += s_red[0][col + w];
     __syncthreads();
   }
   if (tid == 0 && dA_log) {
     const float a = A_log[h];
-    dA_log[h] = (a >= kALogMin && a <= kALogMax) ? s_red[0] : 0.0f;
+    dA_log[h] = (a >= kALogMin && a <= kALogMax) ? s_red[0][0] : 0.0f;
   }
 }
 
@@ -325,14 +420,20 @@ hipError_t launch_gate_bwd(const void* z, const float* A_log, const float* dt_bi
   const int ntile = (T + kGateBwdTile - 1) / kGateBwdTile;
   float* part = reinterpret_cast<float*>(workspace);
   if (ntile > 0) {
-    hipLaunchKernelGGL(gate_bwd_tile_kernel<Tin>, dim3((unsigned)(B * H * ntile)), dim3(256), 0, s, (const Tin*)z,
-                       A_log, dt_bias, dg, dz, part, H, T, K, ntile);
+    const uintptr_t al = (uintptr_t)dg | (uintptr_t)dz | (uintptr_t)dt_bias | (uintptr_t)workspace;
+    if (K % 4 == 0 && kGateBwd4Threads % (K / 4) == 0 && (al & 15) == 0 &&
+        ((uintptr_t)z & (4 * sizeof(Tin) - 1)) == 0)
+      hipLaunchKernelGGL(gate_bwd_tile_kernel4<Tin>, dim3((unsigned)(B * H * ntile)), dim3(kGateBwd4Threads), 0, s,
+                         (const Tin*)z, A_log, dt_bias, dg, dz, part, H, T, K, ntile);
+    else
+      hipLaunchKernelGGL(gate_bwd_tile_kernel<Tin>, dim3((unsigned)(B * H * ntile)), dim3(256), 0, s, (const Tin*)z,
+                         A_log, dt_bias, dg, dz, part, H, T, K, ntile);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (dA_log || d_dt_bias)                    // (T = 0: both come out zero)
-    hipLaunchKernelGGL(gate_bwd_reduce_kernel, dim3((unsigned)H), dim3(256), 0, s, part, A_log, dA_log, d_dt_bias, B,
-                       H, K, ntile);
+    hipLaunchKernelGGL(gate_bwd_reduce_kernel, dim3((unsigned)H), dim3(kGateRedCols * kGateRedSlices), 0, s, part,
+                       A_log, dA_log, d_dt_bias, B, H, K, ntile);
   return hipGetLastError();
 }
 

@@ -360,8 +360,10 @@ def test_chunk_bwd_adjoint_workload_sampled_heads():
 
 
 # ----------------------------------------------------------------------------- gate adjoint
+# K = 64 and 256 take the four-channel first pass (K = 256: two column passes in the
+# reduction); K = 24 and 320 (K / 4 does not divide the workgroup) the one-channel pass
 GATE_BWD_CASES = [("f32", 2, 3, 300, 64), ("bf16", 2, 3, 300, 64), ("f32", 1, 2, 17, 24), ("f32", 1, 2, 0, 8),
-                  ("bf16", 1, 2, 513, 320)]
+                  ("bf16", 1, 2, 513, 320), ("f32", 1, 2, 70, 256)]
 
 
 def _gate_bwd_inputs(B, H, T, K, dtype, seed=23):

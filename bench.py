@@ -207,12 +207,38 @@ def decode_bench(B, steps, warmup, H=32, K=128, V=128):
     b.record(stream)
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / steps
+    # The same steps replayed from a HIP graph of 50 consecutive steps (no host launch per
+    # step): what a serving loop that captures its decode steps sees.
+    ng = 50
+    step = lambda: kda.recurrent_step(q, k, v, z, A_log, dt_bias, beta, S, out=o)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(ng):
+            step()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // ng)
+    a.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us_graph = a.elapsed_time(b) * 1e3 / (reps * ng)
     nbytes = B * H * (2 * K * V * 4 + (3 * K + 2 * V + 1) * 2)
     print(json.dumps({"metric": "decode step state bandwidth (kda_recurrent_step)", "value": round(nbytes / us / 1e3, 1),
                       "unit": "GB/s", "frac_of_8TBps": round(nbytes / us / 1e3 / 8000.0, 4), "us_per_step": round(us, 2),
+                      "graph_us_per_step": round(us_graph, 2),
+                      "graph_GBps": round(nbytes / us_graph / 1e3, 1),
                       "bytes_per_step": nbytes, "steps": steps,
                       "config": {"B": B, "H": H, "K": K, "V": V, "activations": "bf16", "state": "f32"},
-                      "note": "HIP events around the launches; includes launch gaps when the host is slower"}))
+                      "note": "HIP events around the launches (includes launch gaps when the host is slower); "
+                              "graph_*: the same steps replayed from a captured graph of %d steps" % ng}))
 
 
 def gate_bench(steps, warmup):

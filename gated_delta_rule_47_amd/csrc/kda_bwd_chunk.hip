@@ -72,7 +72,10 @@ struct Rec {
   static constexpr int SIZE = round_up(FLAG + 1, 64);
 };
 
-// Workspace layout (bytes), shared by the host and the kernels.
+// Workspace layout (bytes), shared by the host and the kernels.  The per-chunk tensors
+// with value columns (the checkpoint and the chunk-end cotangent, K x VP; U, Y and dZ,
+// C x VP) are stored by value tile: [chunk][VP / 16][rows][16], so that the sequential
+// passes, one workgroup per 16-column tile, write each of them as one contiguous block.
 struct Layout {
   size_t rec, ck, dse, u, y, dz, bytes;
 };
@@ -89,6 +92,11 @@ __host__ __device__ inline Layout layout(int KD, int VP, long long BH, int nck) 
   l.dz = al(l.y + nchunks * C * VP * 4);
   l.bytes = al(l.dz + nchunks * C * VP * 4);
   return l;
+}
+
+// Offset of (row, column col) in a per-chunk [VP / 16][rows][16] tensor of `rows` rows.
+__host__ __device__ __forceinline__ size_t vt_off(int rows, int row, int col) {
+  return ((size_t)(col >> 4) * rows + row) * 16 + (col & 15);
 }
 
 __device__ __forceinline__ float gate_g(float z, float db, float gm) { return -gm * softplus_f(z + db, true); }
@@ -373,7 +381,8 @@ __device__ __forceinline__ void fwd_pass(float* __restrict__ lds, int vt, int bh
     // checkpoint: the state at the chunk start
     for (int i = tid; i < KD * 4; i += 256) {
       const int ch = i >> 2, j = 4 * (i & 3);
-      *reinterpret_cast<float4*>(ck + (chunk * KD + ch) * VP + v0 + j) = *reinterpret_cast<const float4*>(sS + ch * 16 + j);
+      *reinterpret_cast<float4*>(ck + chunk * KD * VP + vt_off(KD, ch, v0 + j)) =
+          *reinterpret_cast<const float4*>(sS + ch * 16 + j);
     }
     __syncthreads();
     if (c + 1 < nck) issue(c + 1);
@@ -396,7 +405,7 @@ __device__ __forceinline__ void fwd_pass(float* __restrict__ lds, int vt, int bh
       for (int i = tid; i < C * 16; i += 256) {
         const int t = i >> 4, j = i & 15;
         const float y = sZ[i] - sPart[i] - sPart[C * 16 + i];
-        yb[(chunk * C + t) * VP + v0 + j] = y;
+        yb[chunk * C * VP + vt_off(C, t, v0 + j)] = y;
         sZ[i] = sBeta[t] * y;
       }
       __syncthreads();
@@ -411,10 +420,16 @@ __device__ __forceinline__ void fwd_pass(float* __restrict__ lds, int vt, int bh
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * rt + 4 * (lane >> 4) + r, j = lane & 15;
           sU[t * 16 + j] = acc[r];
-          ub[(chunk * C + t) * VP + v0 + j] = acc[r];
         }
       }
       __syncthreads();
+      // U for the gradient kernel: the tile's C x 16 block in one contiguous 16-byte-per-lane
+      // copy by the waves that did not compute it
+      if (tid >= 128) {
+        const int i = tid - 128;
+        *reinterpret_cast<float4*>(ub + chunk * C * VP + vt_off(C, 0, v0) + 4 * i) =
+            *reinterpret_cast<const float4*>(sU + 4 * i);
+      }
       // S = diag(D0) (S~ + KR^T U)
       for (int ct = wave; ct < KD / 16; ct += 4) {
         floatx4 acc;
@@ -535,7 +550,8 @@ __device__ __forceinline__ void rev_pass(float* __restrict__ lds, int vt, int bh
     // the chunk-end cotangent, for the gradient kernel
     for (int i = tid; i < KD * 4; i += 256) {
       const int ch = i >> 2, j = 4 * (i & 3);
-      *reinterpret_cast<float4*>(dse + (chunk * KD + ch) * VP + v0 + j) = *reinterpret_cast<const float4*>(sD + ch * 16 + j);
+      *reinterpret_cast<float4*>(dse + chunk * KD * VP + vt_off(KD, ch, v0 + j)) =
+          *reinterpret_cast<const float4*>(sD + ch * 16 + j);
     }
     __syncthreads();
     if (c > 0) issue(c - 1);
@@ -578,11 +594,16 @@ __device__ __forceinline__ void rev_pass(float* __restrict__ lds, int vt, int bh
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * rt + 4 * (lane >> 4) + r, j = lane & 15;
           sDZ[t * 16 + j] = acc[r];
-          dzb[(chunk * C + t) * VP + v0 + j] = acc[r];
           if (t < nval && v0 + j < V) dv[(row0 + t) * V + v0 + j] = sBeta[t] * acc[r];
         }
       }
       __syncthreads();
+      // dZ for the gradient kernel, copied as U is in the forward pass
+      if (tid >= 128) {
+        const int i = tid - 128;
+        *reinterpret_cast<float4*>(dzb + chunk * C * VP + vt_off(C, 0, v0) + 4 * i) =
+            *reinterpret_cast<const float4*>(sDZ + 4 * i);
+      }
       // dS = diag(G0) (dX + QE^T dO - KE^T diag(beta) dZ); a wave reads and writes only the
       // rows of its own tiles of dS
       for (int ct = wave; ct < KD / 16; ct += 4) {
@@ -757,7 +778,7 @@ grad_kernel(const float* __restrict__ d_o, const char* __restrict__ ws, float sc
   float4 rDO, rDZ, rU, rY, rCK[NCH], rDS[NCH];
   auto load_tok = [&](int v0) __attribute__((always_inline)) {
     if (tid < 256) {
-      const size_t g = (size_t)st_t * VP + v0 + 4 * st_f;
+      const size_t g = vt_off(C, st_t, v0 + 4 * st_f);
       const bool ok = st_t < nval && v0 + 4 * st_f < V;
       rDO = ok ? ld4(d_o + (row0 + st_t) * V + v0 + 4 * st_f) : make_float4(0.f, 0.f, 0.f, 0.f);
       rDZ = ld4(dzp + g);
@@ -770,7 +791,7 @@ grad_kernel(const float* __restrict__ d_o, const char* __restrict__ ws, float sc
     for (int m = 0; m < NCH; ++m) {
       const int i = tid + 512 * m;
       if (i < KD * 8) {
-        const size_t off = (size_t)(i >> 3) * VP + v0 + 4 * (i & 7);
+        const size_t off = vt_off(KD, i >> 3, v0 + 4 * (i & 7));
         rCK[m] = ld4(ckp + off);
         rDS[m] = ld4(dsep + off);
       }
@@ -1048,9 +1069,9 @@ grad_token_kernel(const float* __restrict__ q, const float* __restrict__ k, cons
       __syncthreads();
     };
     __syncthreads();                            // (the previous chunk is done with sD)
-    for (int i = tid; i < KD * VP; i += 512) sD[i] = dsep[i];
+    for (int i = tid; i < KD * VP; i += 512) sD[i] = dsep[vt_off(KD, i / VP, i % VP)];
     for (int t = nval - 1; t >= 0; --t) {
-      for (int i = tid; i < KD * VP; i += 512) sS[i] = ckp[i];
+      for (int i = tid; i < KD * VP; i += 512) sS[i] = ckp[vt_off(KD, i / VP, i % VP)];
       __syncthreads();
       for (int u = 0; u < t; ++u) {
         load_token(u);

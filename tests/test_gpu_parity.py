@@ -407,6 +407,29 @@ def test_gate_bwd(dtype, B, H, T, K):
         assert torch.equal(dzi, dz)
 
 
+@pytest.mark.parametrize("K", [64, 10])
+def test_gate_and_gate_bwd_without_bias_or_alpha(K):
+    """No dt_bias (a null pointer: zero bias) and no alpha output, through both gate
+    kernels (K = 64: four channels per thread; K = 10: one channel) and both first
+    passes of the gate adjoint; the same against the oracle with a zero bias."""
+    rng = np.random.default_rng(41)
+    B, H, T = 2, 3, 45
+    z = (rng.standard_normal((B, H, T, K)) * 4).astype(np.float32)
+    A_log = np.array([-3.0, 0.5, 25.0], dtype=np.float32)
+    dg = rng.standard_normal((B, H, T, K)).astype(np.float32)
+    zero = np.zeros((H, K), dtype=np.float32)
+    zd, Ad, dgd = to_dev(z, torch.float32), to_dev(A_log, torch.float32), to_dev(dg, torch.float32)
+    g, a = kda.gate(zd, Ad, None, want_alpha=False)
+    assert a is None
+    gr, _ = R.gate(z, A_log, zero)
+    _check("g", host(g), gr, 2e-6)
+    dz, dA, ddb = kda.gate_bwd(zd, Ad, None, dgd)
+    dzr, dAr, ddbr = R.gate_adjoint(z, A_log, zero, dg)
+    _check("dz", host(dz), dzr, 2e-6)
+    _check("dA_log", host(dA), dAr, 1e-4)
+    _check("d_dt_bias", host(ddb), ddbr, 1e-4)
+
+
 def test_gate_bwd_after_chunk_bwd_end_to_end():
     """The training chain: the adjoint's dg fed to the gate adjoint gives dz, dA_log and
     d dt_bias of sum(o * d_o); the oracle runs the same chain in f64."""

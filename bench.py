@@ -551,8 +551,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         workers = min(16, len(os.sched_getaffinity(0)))
-        print("bench: CPU oracle baseline on %d heads" % workers, file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, n_heads=workers, workers=workers, scalar_gate=args.scalar_gate)
+        # two whole heads per worker: about 20 s of CPU work at the long workload
+        print("bench: CPU oracle baseline on %d heads" % (2 * workers), file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, n_heads=2 * workers, workers=workers, scalar_gate=args.scalar_gate)
     out = {
         "metric": ((METRIC_NORM if args.norm else METRIC_SCALAR if args.scalar_gate else METRIC) if wl.name == "long"
                    else "KDA chunked-forward tokens/s (B·H·T/s), %s workload%s"

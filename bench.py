@@ -132,7 +132,8 @@ def copy_bandwidth_gbs(torch, mib: int = 1024, launches: int = 10) -> float:
 
 
 def cpu_baseline(wl, n_heads: int, workers: int, scalar_gate: bool = False) -> dict:
-    """The f64 oracle (gate + token recurrence) on n_heads whole heads, one per process:
+    """The f64 oracle (gate + token recurrence) on n_heads whole heads, one per task of a pool
+    of `workers` processes:
     head-tokens per second of wall time from the first head's start to the last head's
     end (input generation excluded)."""
     heads = [(i // wl.H % wl.B, i % wl.H) for i in range(n_heads)]
@@ -142,8 +143,8 @@ def cpu_baseline(wl, n_heads: int, workers: int, scalar_gate: bool = False) -> d
     cpu = sum(e - s for s, e in spans)
     return {"value": n_heads * wl.T / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
             "cpu_model": cpu_model(), "host_cores": os.cpu_count(),
-            "sample": "%d of %d heads at full T=%d (f64 numpy token recurrence, one head per process; "
-                      "%.1f s wall, %.1f s of CPU work)" % (n_heads, wl.B * wl.H, wl.T, wall, cpu)}
+            "sample": "%d of %d heads at full T=%d (f64 numpy token recurrence, one head per task on %d worker "
+                      "processes; %.1f s wall, %.1f s of CPU work)" % (n_heads, wl.B * wl.H, wl.T, workers, wall, cpu)}
 
 
 def _pmc_per_dispatch(directory: str, counter: str, kernel_match: str) -> list:
